@@ -1,0 +1,263 @@
+"""CPU oracle of the DFlash2 block-draft candidate step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+run this module: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP library.
+
+Plain numpy, float64 arithmetic throughout (the pages fix no accumulation
+precision; float64 makes the oracle the definition up to rounding), with one
+rounding at each point where the method's data type is narrower than that:
+
+* bf16 inputs are widened exactly;
+* LM-head logits are an fp32 number whose bf16 rounding is the top-k key
+  (see ``lm_topk``);
+* bf16 outputs (q/k after norm + RoPE, attention output) are rounded once,
+  float64 -> fp32 -> bf16, each step round-to-nearest-even.
+
+Sources (vLLM API docs of ``vllm.models.beam.nvidia.dflash2`` and of the DFlash
+speculator ``vllm.v1.worker.gpu.spec_decode.dflash.speculator``):
+
+* ``DFlash2BeamForCausalLM.compute_candidates`` and its ``LogitsProcessor``
+  (``scale=output_multiplier``, ``soft_cap=final_logit_softcapping``, a cap of
+  zero or less means none) -> ``lm_topk``;
+* ``DFlash2BeamCandidateSelector`` (class docstring: edge score = candidate's
+  own logit + <predecessor[q] * h_p, successor[c]>, predecessor of the first
+  position = the anchor token; ``forward``: output ``[requests, steps, top_k,
+  top_k]``; ``hidden_projection`` = bias-free ``hidden -> rank`` linear)
+  -> ``candidate_edges``;
+* ``DFlash2BeamAttention.forward`` (per-head q/k RMSNorm, NeoX RoPE, slot-mapped
+  K/V cache write) -> ``qk_norm_rope_cache``;
+* ``DFlash2BeamAttention.__init__`` (every layer non-causal sliding-window
+  attention, scale ``head_dim ** -0.5``, GQA) and the speculator's query block of
+  one anchor plus N mask tokens per request -> ``block_attn``.
+
+Where the pages leave a step open, the reading taken is stated in the function.
+Parity pins for every function live in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "f64_to_bf16", "f64_to_f32", "lm_logit_keys", "lm_topk",
+    "candidate_edges", "qk_norm_rope_cache", "block_attn", "attention_window",
+]
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers (own implementation: bit manipulation on IEEE fp32)
+# --------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact: a bf16 is the top half of an fp32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f64_to_f32(x: np.ndarray) -> np.ndarray:
+    """float64 -> float32, round to nearest even (numpy's IEEE cast)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def f32_to_bf16(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest, ties to even.  NaN stays a
+    quiet NaN."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    r = np.where(nan, (u >> np.uint32(16)) | np.uint32(0x40), r)
+    return r.astype(np.uint16)
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> fp32 -> bf16 bits (each step round to nearest even)."""
+    return f32_to_bf16(f64_to_f32(x))
+
+
+# --------------------------------------------------------------------------
+# LM-head top-k
+# --------------------------------------------------------------------------
+def lm_logit_keys(H: np.ndarray, W: np.ndarray, multiplier: float, softcap: float,
+                  rows=None, vocab_chunk: int = 16384) -> np.ndarray:
+    """bf16 key of every logit: ``key[t, v]`` as bf16 bits, rows ``rows`` of H.
+
+    logit = multiplier * <H[t], W[v]> (float64 dot product of the widened bf16
+    values); then, when ``softcap > 0``, ``softcap * tanh(logit / softcap)``.
+    The logit is an fp32 number and the key its bf16 rounding.
+
+    Readings (the pages show only the processor's constructor arguments):
+    scale first, cap last; cap function ``c * tanh(x / c)``; the key is the
+    LM head's output dtype (bf16).
+    """
+    Hs = H if rows is None else H[np.asarray(rows)]
+    h = bf16_to_f64(Hs)
+    V = W.shape[0]
+    keys = np.empty((h.shape[0], V), dtype=np.uint16)
+    for v0 in range(0, V, vocab_chunk):
+        w = bf16_to_f64(W[v0:v0 + vocab_chunk])
+        x = multiplier * (h @ w.T)
+        if softcap > 0:
+            x = softcap * np.tanh(x / softcap)
+        keys[:, v0:v0 + w.shape[0]] = f64_to_bf16(x)
+    return keys
+
+
+def topk_from_keys(keys: np.ndarray, k: int):
+    """Top ``k`` of each row by (key value descending, token id ascending).
+
+    A stable full sort of every row: the plain definition of the selection,
+    with the tie rule (lower token id first) deciding membership at the k-th
+    place as well as the order.  -0 and +0 compare equal (they are the same
+    value).  Returns (ids int32 [T,k], values fp32 [T,k]).
+    """
+    vals = bf16_to_f64(keys)
+    T, V = vals.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    out = np.empty((T, k), dtype=np.float32)
+    col = np.arange(V)
+    for t in range(T):
+        order = np.lexsort((col, -vals[t]))  # last key is primary
+        ids[t] = order[:k]
+        out[t] = vals[t, order[:k]].astype(np.float32)
+    return ids, out
+
+
+def lm_topk(H, W, k: int, multiplier: float = 1.0, softcap: float = 0.0, rows=None):
+    """``compute_candidates``: the top-k token ids of each hidden state under the
+    shared LM head, and their logits (bf16 keys widened to fp32)."""
+    return topk_from_keys(lm_logit_keys(H, W, multiplier, softcap, rows), k)
+
+
+# --------------------------------------------------------------------------
+# Candidate-selector edge scores
+# --------------------------------------------------------------------------
+def candidate_edges(P, S, ids, U, H, Wp, anchor) -> np.ndarray:
+    """Edge scores ``E[r, p, q, c]`` (fp32, ``[requests, steps, k, k]``).
+
+    h_p = Wp . h_{r,p}  (the bias-free hidden -> rank projection, float64);
+    pred(r, 0, q) = anchor[r] for every q, pred(r, p, q) = ids[r, p-1, q];
+    E[r,p,q,c] = U[r,p,c] + sum_i P[pred,i] * h_p[i] * S[ids[r,p,c], i].
+
+    ``P``, ``S``: bf16 ``[vocab, rank]``; ``ids`` int ``[Rq, steps, k]``;
+    ``U`` fp32 ``[Rq, steps, k]``; ``H`` bf16 ``[Rq*steps, hidden]`` (row
+    ``r*steps + p``); ``Wp`` bf16 ``[rank, hidden]``; ``anchor`` int ``[Rq]``.
+    """
+    Rq, St, k = ids.shape
+    R = P.shape[1]
+    hp = (bf16_to_f64(H) @ bf16_to_f64(Wp).T).reshape(Rq, St, R)
+    pred = np.empty_like(ids)
+    pred[:, 0, :] = np.asarray(anchor)[:, None]
+    pred[:, 1:, :] = ids[:, :-1, :]
+    Pf = bf16_to_f64(P)
+    Sf = bf16_to_f64(S)
+    a = Pf[pred] * hp[:, :, None, :]          # [Rq, St, k(q), R]
+    b = Sf[ids]                               # [Rq, St, k(c), R]
+    bil = np.einsum("rpqi,rpci->rpqc", a, b)
+    E = np.asarray(U, dtype=np.float64)[:, :, None, :] + bil
+    return E.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# q/k RMSNorm + NeoX RoPE + slot-mapped K/V cache write
+# --------------------------------------------------------------------------
+def rope_angles(positions: np.ndarray, D: int, theta: float) -> np.ndarray:
+    """angle[t, i] = pos_t * theta ** (-2 i / D), i < D/2 (float64)."""
+    i = np.arange(D // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / D)
+    return np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+
+
+def _rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """x * (mean(x^2) + eps)^-1/2 * w over the last axis (plain weight w)."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * w
+
+
+def _neox_rotate(y: np.ndarray, ang: np.ndarray) -> np.ndarray:
+    """Rotate pairs (i, i + D/2) of the last axis by ``ang`` (NeoX style)."""
+    D = y.shape[-1]
+    h = D // 2
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = y[..., :h], y[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float,
+                       positions, theta: float, slots=None, cache=None,
+                       block_size: int = 16):
+    """Draft layer's fused q/k norm + RoPE + cache write.
+
+    ``qkv``: bf16 ``[T, (Hq + 2 Hkv) D]``, q heads, then k heads, then v heads.
+    For each token and head: RMSNorm over the head (weights ``q_w``/``k_w``,
+    one eps for both), then NeoX RoPE at the token's position (rotary dim =
+    head dim), one bf16 rounding at the output.  With a cache, token t with
+    ``slots[t] >= 0`` writes K' to ``cache[slot // bs, h, slot % bs, :D]`` and
+    its V bits unchanged to ``[..., D:]``; negative slots write nothing.
+
+    Returns ``(q_out bf16 [T,Hq,D], k_out bf16 [T,Hkv,D], cache_out or None)``.
+    """
+    qkv = np.asarray(qkv)
+    T = qkv.shape[0]
+    x = bf16_to_f64(qkv).reshape(T, Hq + 2 * Hkv, D)
+    ang = rope_angles(positions, D, theta)[:, None, :]  # [T,1,D/2]
+    q = _neox_rotate(_rms_norm(x[:, :Hq], bf16_to_f64(q_w), eps), ang)
+    k = _neox_rotate(_rms_norm(x[:, Hq:Hq + Hkv], bf16_to_f64(k_w), eps), ang)
+    q_out = f64_to_bf16(q)
+    k_out = f64_to_bf16(k)
+    cache_out = None
+    if cache is not None and slots is not None:
+        cache_out = np.array(cache, copy=True)
+        v_bits = qkv.reshape(T, Hq + 2 * Hkv, D)[:, Hq + Hkv:]
+        for t in range(T):
+            s = int(slots[t])
+            if s < 0:
+                continue
+            b, o = divmod(s, block_size)
+            cache_out[b, :, o, :D] = k_out[t]
+            cache_out[b, :, o, D:] = v_bits[t]
+    return q_out, k_out, cache_out
+
+
+# --------------------------------------------------------------------------
+# Non-causal sliding-window block attention over a paged cache
+# --------------------------------------------------------------------------
+def attention_window(seq_len: int, Lq: int, i: int, window: int):
+    """Visible key positions ``[lo, hi)`` of query ``i`` of a request.
+
+    Reading: query i (0 = the anchor) sits at position ``seq_len - Lq + i``;
+    attention is non-causal inside the block, so every key of the request up to
+    ``seq_len - 1`` is visible above, and the sliding window keeps the
+    ``window`` keys at or before the query's position below.
+    """
+    pos = seq_len - Lq + i
+    return max(0, pos - window + 1), seq_len
+
+
+def block_attn(q, cache, block_tables, seq_lens, Lq: int, Hq: int, Hkv: int,
+               D: int, block_size: int, window: int, scale: float) -> np.ndarray:
+    """``o = softmax(q K^T * scale) V`` per (request, q head, query), float64,
+    over the visible keys (``attention_window``), K/V gathered through the
+    block table; kv head = q head // (Hq / Hkv).  Output bf16 ``[Rq*Lq, Hq, D]``.
+    """
+    Rq = len(seq_lens)
+    group = Hq // Hkv
+    qf = bf16_to_f64(q).reshape(Rq, Lq, Hq, D)
+    out = np.empty((Rq, Lq, Hq, D), dtype=np.float64)
+    for r in range(Rq):
+        L = int(seq_lens[r])
+        lo0, _ = attention_window(L, Lq, 0, window)
+        kpos = np.arange(lo0, L)
+        phys = np.asarray(block_tables[r])[kpos // block_size]
+        rows = cache[phys, :, kpos % block_size, :]            # [nk, Hkv, 2D]
+        Kf = bf16_to_f64(rows[:, :, :D])
+        Vf = bf16_to_f64(rows[:, :, D:])
+        for i in range(Lq):
+            lo, hi = attention_window(L, Lq, i, window)
+            sel = slice(lo - lo0, hi - lo0)
+            for h in range(Hq):
+                kh = h // group
+                s = Kf[sel, kh, :] @ qf[r, i, h] * scale
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                out[r, i, h] = p @ Vf[sel, kh, :]
+    return f64_to_bf16(out.reshape(Rq * Lq, Hq, D))

@@ -1,0 +1,261 @@
+"""Seeded synthetic inputs for the DFlash2 block-draft candidate step.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic.  The CPU oracle (``oracle/``) and the HIP library's tests
+and benchmark both take their inputs from here, so the two sides see the same
+bits.
+
+Shapes follow the workloads of the DFlash2 drafter (vLLM API docs,
+``vllm.models.beam.nvidia.dflash2``): hidden states ``[requests*steps,
+hidden]`` through the shared LM head ``[vocab, hidden]`` (``DFlash2BeamForCausalLM``),
+codebooks ``[vocab, rank]`` and a ``hidden -> rank`` projection
+(``DFlash2BeamCandidateSelector.__init__``), a fused ``qkv`` row per query token
+(``DFlash2BeamAttention.forward``) and a paged K/V cache.
+
+Every bf16 tensor is returned as ``numpy.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Workload table.  Sizes are the five synthetic workloads of the candidate
+# step; values the workloads leave open are marked "chosen".
+# --------------------------------------------------------------------------
+CONFIGS = {
+    "tiny": dict(
+        requests=2, steps=4, top_k=4, vocab=1024, hidden=256, rank=16,
+        softcap=0.0, multiplier=1.0, seed=101,
+    ),
+    "mid": dict(
+        requests=32, steps=8, top_k=8, vocab=32768, hidden=2048, rank=64,
+        softcap=30.0, multiplier=1.0, seed=102,
+        # draft-layer q/k-norm + RoPE + cache write at this size
+        qk=dict(hq=16, hkv=4, head_dim=128, query_len=9, cache_slots=4096,
+                block_size=16,          # chosen (same as the attention workload)
+                eps=1e-6, theta=1e6,    # chosen (same as the attention workload)
+                ctx_lo=512, ctx_hi=4096),  # chosen: context length per request
+    ),
+    "full": dict(
+        requests=256, steps=16, top_k=16, vocab=151936, hidden=4096, rank=128,
+        softcap=30.0, multiplier=0.5, seed=103,
+    ),
+    "attn": dict(
+        requests=128, query_len=16, hq=32, hkv=8, head_dim=128, window=2048,
+        ctx_lo=512, ctx_hi=8192, block_size=16, eps=1e-6, theta=1e6, seed=104,
+    ),
+    "large": dict(
+        requests=512, steps=16, top_k=32, vocab=262144, hidden=5120, rank=256,
+        softcap=30.0, multiplier=1.0,  # multiplier chosen: the workload names none
+        seed=105, lm_mantissa_bits=4,
+    ),
+}
+
+SIGMA_W = 0.02  # N(0, 0.02) init of the LM head, codebooks and projection
+
+_CHUNK = 1 << 22  # elements per independent random stream (fixed: results do not
+                  # depend on the number of threads)
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _fill_chunks(seed: int, stream: int, n: int, sigma: float, out: np.ndarray,
+                 convert=None) -> None:
+    """Fill ``out`` (length ``n``) with N(0, sigma^2) draws.
+
+    Chunk ``i`` of ``_CHUNK`` elements comes from its own PCG64 stream,
+    ``SeedSequence([seed, stream, i])``, so the values are fixed by
+    (seed, stream) whatever the number of threads.  ``convert`` maps a float32
+    chunk to ``out``'s dtype.
+    """
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+
+    def fill(i: int) -> None:
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, i])))
+        buf = g.standard_normal(hi - lo, dtype=np.float32)
+        if sigma != 1.0:
+            buf *= np.float32(sigma)
+        out[lo:hi] = buf if convert is None else convert(buf)
+
+    if nchunks <= 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+
+
+def normal_f32(seed: int, stream: int, n: int, sigma: float = 1.0) -> np.ndarray:
+    """``n`` float32 draws of N(0, sigma^2) (see ``_fill_chunks``)."""
+    out = np.empty(n, dtype=np.float32)
+    _fill_chunks(seed, stream, n, sigma, out)
+    return out
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (round to nearest even), via torch's cast."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_normal(seed: int, stream: int, shape, sigma: float = 1.0) -> np.ndarray:
+    """N(0, sigma^2) draws rounded to bf16 (bit patterns); the float32 draws are
+    the same as ``normal_f32(seed, stream, ...)``."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    _fill_chunks(seed, stream, n, sigma, out, convert=to_bf16_bits)
+    return out.reshape(shape)
+
+
+def keep_mantissa_bits(bits: np.ndarray, m: int) -> np.ndarray:
+    """Round bf16 values (bit patterns) to ``m`` explicit mantissa bits, ties to
+    even.  Used to make LM-head logits tie-heavy in the large-vocab workload."""
+    drop = 7 - m
+    if drop <= 0:
+        return bits
+    u = bits.astype(np.uint32)
+    half = np.uint32(1 << (drop - 1))
+    lsb = (u >> np.uint32(drop)) & np.uint32(1)
+    r = ((u + half - np.uint32(1) + lsb) >> np.uint32(drop)) << np.uint32(drop)
+    keep_special = (u & np.uint32(0x7F80)) == np.uint32(0x7F80)  # inf / nan untouched
+    r = np.where(keep_special, u, r)
+    return (r & np.uint32(0xFFFF)).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Candidate head (LM-head top-k and edge scores)
+# --------------------------------------------------------------------------
+def candidate_inputs(name: str, requests: int | None = None) -> dict:
+    """Inputs of the LM-head top-k and the candidate edges for workload ``name``.
+
+    Draw order (streams): 0 hidden states, 1 LM head, 2 predecessor codebook,
+    3 successor codebook, 4 projection, 5 anchors, 6 candidate ids, 7 unary
+    logits.  ``requests`` may shrink the batch (the first rows of the full draw
+    are kept, so a smaller batch is a prefix of the full one).
+    """
+    c = CONFIGS[name]
+    seed = c["seed"]
+    R_full, S, k, V, Hd, R = (c["requests"], c["steps"], c["top_k"], c["vocab"],
+                              c["hidden"], c["rank"])
+    Rq = R_full if requests is None else int(requests)
+    T_full = R_full * S
+    H = bf16_normal(seed, 0, (T_full, Hd))[: Rq * S].copy()
+    W = bf16_normal(seed, 1, (V, Hd), SIGMA_W)
+    if c.get("lm_mantissa_bits"):
+        W = keep_mantissa_bits(W, c["lm_mantissa_bits"])
+    P = bf16_normal(seed, 2, (V, R), SIGMA_W)
+    Sc = bf16_normal(seed, 3, (V, R), SIGMA_W)
+    Wp = bf16_normal(seed, 4, (R, Hd), SIGMA_W)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 5])))
+    anchor = g.integers(0, V, size=R_full, dtype=np.int64).astype(np.int32)[:Rq].copy()
+    # Candidate ids for the edge stage on its own: k distinct ids per position.
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 6])))
+    ids = np.empty((R_full, S, k), dtype=np.int32)
+    for t in range(R_full * S):
+        ids.reshape(-1, k)[t] = g.choice(V, size=k, replace=False)
+    ids = ids[:Rq].copy()
+    # Unary logits: the scale of real LM-head logits (std ~ 0.02*sqrt(hidden)).
+    U = normal_f32(seed, 7, R_full * S * k, SIGMA_W * math.sqrt(Hd)).reshape(R_full, S, k)[:Rq].copy()
+    return dict(H=H, W=W, P=P, S=Sc, Wp=Wp, anchor=anchor, ids=ids, U=U,
+                requests=Rq, steps=S, top_k=k, vocab=V, hidden=Hd, rank=R,
+                softcap=c["softcap"], multiplier=c["multiplier"])
+
+
+# --------------------------------------------------------------------------
+# Draft-layer q/k-norm + RoPE + cache write, and block attention
+# --------------------------------------------------------------------------
+def _paged_layout(g: np.random.Generator, seq_lens: np.ndarray, block_size: int):
+    nblk_per = (seq_lens + block_size - 1) // block_size
+    total = int(nblk_per.sum())
+    perm = g.permutation(total).astype(np.int32)
+    max_blocks = int(nblk_per.max())
+    tables = np.zeros((len(seq_lens), max_blocks), dtype=np.int32)
+    off = 0
+    for r, n in enumerate(nblk_per):
+        tables[r, :n] = perm[off:off + n]
+        off += n
+    return tables, total
+
+
+def attention_inputs(name: str = "attn", requests: int | None = None,
+                     q_scale: float = 1.0) -> dict:
+    """Paged-cache attention inputs (and the qkv rows of the query block).
+
+    Context lengths ``ctx_r`` are uniform integers in ``[ctx_lo, ctx_hi]``; the
+    query block of request r holds tokens ``ctx_r .. ctx_r+Lq-1`` and
+    ``seq_lens[r] = ctx_r + Lq``.  Physical cache blocks are a random
+    permutation, scattered into the block tables.  Cache K and V, the queries and
+    the qkv rows are N(0,1) bf16; ``q_scale`` multiplies the queries before
+    rounding (a peaked-softmax variant).
+    """
+    c = CONFIGS[name]
+    seed = c["seed"]
+    Rq_full, Lq, Hq, Hkv, D, bs = (c["requests"], c["query_len"], c["hq"], c["hkv"],
+                                   c["head_dim"], c["block_size"])
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0])))
+    ctx = g.integers(c["ctx_lo"], c["ctx_hi"] + 1, size=Rq_full, dtype=np.int64)
+    Rq = Rq_full if requests is None else int(requests)
+    ctx = ctx[:Rq].copy()
+    seq = (ctx + Lq).astype(np.int32)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1])))
+    tables, nblk = _paged_layout(g, seq.astype(np.int64), bs)
+    cache = bf16_normal(seed, 2, (nblk, Hkv, bs, 2 * D))
+    qf = normal_f32(seed, 3, Rq * Lq * Hq * D)
+    if q_scale != 1.0:
+        qf *= np.float32(q_scale)
+    q = to_bf16_bits(qf).reshape(Rq * Lq, Hq, D)
+    qkv = bf16_normal(seed, 4, (Rq * Lq, (Hq + 2 * Hkv) * D))
+    gw = normal_f32(seed, 5, 2 * D, 0.1) + np.float32(1.0)
+    q_w = to_bf16_bits(gw[:D])
+    k_w = to_bf16_bits(gw[D:])
+    positions = (ctx[:, None] + np.arange(Lq)[None, :]).reshape(-1).astype(np.int64)
+    blk = tables[np.repeat(np.arange(Rq), Lq), positions // bs].astype(np.int64)
+    slots = blk * bs + positions % bs
+    return dict(q=q, cache=cache, block_tables=tables, seq_lens=seq, ctx=ctx,
+                qkv=qkv, q_w=q_w, k_w=k_w, positions=positions, slots=slots,
+                requests=Rq, query_len=Lq, hq=Hq, hkv=Hkv, head_dim=D,
+                block_size=bs, window=c["window"], eps=c["eps"], theta=c["theta"],
+                num_blocks=nblk, max_pos=int(positions.max()) + 1)
+
+
+def qk_inputs(name: str = "mid", pad_fraction: float = 0.0) -> dict:
+    """Inputs of the fused q/k-norm + RoPE + cache write for workload ``name``
+    (``mid``: slots are the first ``T_q`` entries of a random permutation of the
+    cache's slots; ``pad_fraction`` of them are set to -1, the skip value)."""
+    c = CONFIGS[name]
+    qc = c["qk"]
+    seed = c["seed"] + 1000
+    Rq, Lq, Hq, Hkv, D = c["requests"], qc["query_len"], qc["hq"], qc["hkv"], qc["head_dim"]
+    bs = qc["block_size"]
+    Tq = Rq * Lq
+    qkv = bf16_normal(seed, 0, (Tq, (Hq + 2 * Hkv) * D))
+    gw = normal_f32(seed, 1, 2 * D, 0.1) + np.float32(1.0)
+    q_w = to_bf16_bits(gw[:D])
+    k_w = to_bf16_bits(gw[D:])
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2])))
+    ctx = g.integers(qc["ctx_lo"], qc["ctx_hi"], size=Rq, dtype=np.int64)
+    positions = (ctx[:, None] + np.arange(Lq)[None, :]).reshape(-1).astype(np.int64)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3])))
+    slots = g.permutation(qc["cache_slots"])[:Tq].astype(np.int64)
+    if pad_fraction > 0:
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 4])))
+        pad = g.random(Tq) < pad_fraction
+        slots[pad] = -1
+    nblk = qc["cache_slots"] // bs
+    cache = bf16_normal(seed, 5, (nblk, Hkv, bs, 2 * D))
+    return dict(qkv=qkv, q_w=q_w, k_w=k_w, positions=positions, slots=slots,
+                cache=cache, tokens=Tq, hq=Hq, hkv=Hkv, head_dim=D, block_size=bs,
+                num_blocks=nblk, eps=qc["eps"], theta=qc["theta"],
+                max_pos=int(positions.max()) + 1)
