@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash2 block-draft candidate step on one MI355X.
+
+One step = the whole hot path over one synthetic batch, inputs resident in HBM:
+  1. dflash_lm_topk            256 requests x 16 steps, vocab 151936, hidden 4096, top_k 16,
+                               output_multiplier 0.5, softcap 30
+  2. dflash_candidate_edges    the same rows, rank 128, on step 1's ids and logits
+  3. dflash_qk_norm_rope_cache draft-layer query block, 128 requests x 16 tokens, 32/8 heads
+  4. dflash_block_attn         the same block over the paged cache, window 2048,
+                               context lengths uniform in [512, 8192]
+
+Prints one JSON line.  `value` is edge scores per second of the whole step.
+Per-kernel times come from HIP events on the stream the kernels run on; the
+roofline object is for the dominant kernel (the LM-head top-k, MFMA-bound).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "edge scores/s + LM-head top-k GB/s as % of HBM peak, 256 reqs×16 steps"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+LM_SOURCE = os.path.join(ROOT, "block_draft_candidate_amd", "csrc", "lm_topk.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lm_bytes(T, V, Hd, k):
+    return V * Hd * 2 + T * Hd * 2 + T * k * 8
+
+
+def lm_flops(T, V, Hd):
+    return 2 * T * V * Hd
+
+
+def edge_bytes(Rq, S, k, R, Hd):
+    T = Rq * S
+    gathers = Rq * (1 + (S - 1) * k) * R * 2 + Rq * S * k * R * 2
+    return T * Hd * 2 + R * Hd * 2 + gathers + T * k * 4 * 2 + Rq * 4 + T * k * k * 4
+
+
+def qk_bytes(Tq, Hq, Hkv, D):
+    return (Tq * (Hq + 2 * Hkv) * D * 2 + 2 * D * 2 + Tq * 8 * 2 + Tq * D * 4
+            + Tq * Hq * D * 2 + Tq * Hkv * 2 * D * 2)
+
+
+def attn_work(seq_lens, Lq, Hq, Hkv, D, window):
+    """Algorithmic bytes (each visible K/V row once per kv head, q, out) and flops."""
+    import numpy as np
+    L = np.asarray(seq_lens, np.int64)
+    lo0 = np.maximum(0, L - Lq - window + 1)
+    keys = L - lo0
+    nbytes = int(keys.sum()) * Hkv * 2 * D * 2 + 2 * len(L) * Lq * Hq * D * 2
+    vis = 0
+    for i in range(Lq):
+        lo = np.maximum(0, L - Lq + i - window + 1)
+        vis += int((L - lo).sum())
+    flops = 4 * D * Hq * vis
+    return nbytes, flops
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+        src = hashlib.sha256(open(LM_SOURCE, "rb").read()).hexdigest()
+        if rec and rec.get("source_sha256") == src:
+            return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(cand, attn, edges_per_step, steps_per_sample):
+    """The oracle timed on a bounded sample: 2 candidate-head requests (32 rows)
+    and 1 attention request, i.e. 1/128 of the step's work."""
+    import numpy as np
+    from oracle import dflash_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    S, k = cand["steps"], cand["top_k"]
+    rows = np.arange(2 * S)
+    t0 = time.perf_counter()
+    ids, vals = O.lm_topk(cand["H"], cand["W"], k, cand["multiplier"], cand["softcap"], rows=rows)
+    O.candidate_edges(cand["P"], cand["S"], ids.reshape(2, S, k), vals.reshape(2, S, k), cand["H"][rows],
+                      cand["Wp"], cand["anchor"][:2])
+    Lq, D = attn["query_len"], attn["head_dim"]
+    q, _, c2 = O.qk_norm_rope_cache(attn["qkv"][:Lq], attn["hq"], attn["hkv"], D, attn["q_w"], attn["k_w"],
+                                    attn["eps"], attn["positions"][:Lq], attn["theta"], attn["slots"][:Lq],
+                                    attn["cache"], attn["block_size"])
+    O.block_attn(q, c2, attn["block_tables"][:1], attn["seq_lens"][:1], Lq, attn["hq"], attn["hkv"], D,
+                 attn["block_size"], attn["window"], D ** -0.5)
+    dt = time.perf_counter() - t0
+    return {"value": edges_per_step / (dt * steps_per_sample), "unit": "edge scores/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"2 of 256 candidate-head requests (32 rows: LM-head top-k + edges) and 1 of 128 "
+                      f"attention requests (qk-norm/RoPE/cache + attention) = 1/{steps_per_sample} of a step; "
+                      f"{dt:.1f} s on the host, scaled to a whole step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path would shard across GPUs "
+              "as described in DESIGN.md but no multi-GPU run is part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_draft_candidate_amd as B
+    import workloads as WL
+
+    B.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dbf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    log("generating inputs ...")
+    cand = WL.candidate_inputs("full")
+    attn = WL.attention_inputs("attn")
+    Rq, S, k, V, Hd, R = (cand["requests"], cand["steps"], cand["top_k"], cand["vocab"], cand["hidden"],
+                          cand["rank"])
+    T = Rq * S
+    H, W = dbf(cand["H"]), dbf(cand["W"])
+    P, Sc, Wp = dbf(cand["P"]), dbf(cand["S"]), dbf(cand["Wp"])
+    anchor = torch.from_numpy(cand["anchor"]).to(dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    logits = torch.empty((T, k), dtype=torch.float32, device=dev)
+    edges = torch.empty((Rq, S, k, k), dtype=torch.float32, device=dev)
+    ws_lm = torch.empty(B.lm_topk_workspace_size(T, V, Hd, k), dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(B.candidate_edges_workspace_size(T, R, Hd), dtype=torch.uint8, device=dev)
+
+    Lq, Hq, Hkv, D = attn["query_len"], attn["hq"], attn["hkv"], attn["head_dim"]
+    Rq_a = attn["requests"]
+    qkv = dbf(attn["qkv"])
+    q_w, k_w = dbf(attn["q_w"]), dbf(attn["k_w"])
+    positions = torch.from_numpy(attn["positions"]).to(dev)
+    slots = torch.from_numpy(attn["slots"]).to(dev)
+    cache = dbf(attn["cache"])
+    tables = torch.from_numpy(attn["block_tables"]).to(dev)
+    seq_lens = torch.from_numpy(attn["seq_lens"]).to(dev)
+    cos_sin = B.rope_cos_sin(attn["max_pos"], D, attn["theta"], dev)
+    q_out = torch.empty((Rq_a * Lq, Hq, D), dtype=torch.bfloat16, device=dev)
+    a_out = torch.empty_like(q_out)
+    torch.cuda.synchronize()
+
+    names = ["lm_topk", "edges", "qk", "attn"]
+    ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+    acc_ms = {n: 0.0 for n in names}
+
+    def step(timed):
+        def call(n, fn):
+            if timed:
+                ev[n][0].record()
+            fn()
+            if timed:
+                ev[n][1].record()
+        call("lm_topk", lambda: B.lm_topk(H, W, k, cand["multiplier"], cand["softcap"], ids, logits, ws_lm))
+        call("edges", lambda: B.candidate_edges(P, Sc, ids.view(Rq, S, k), logits.view(Rq, S, k), H, Wp, anchor,
+                                                edges, ws_e))
+        call("qk", lambda: B.qk_norm_rope_cache(qkv, Hq, Hkv, D, q_w, k_w, attn["eps"], positions, cos_sin,
+                                                slots, cache, q_out=q_out, want_k=False))
+        call("attn", lambda: B.block_attn(q_out, cache, tables, seq_lens, Lq, attn["window"], out=a_out))
+        if timed:
+            torch.cuda.synchronize()
+            for n in names:
+                acc_ms[n] += ev[n][0].elapsed_time(ev[n][1])
+
+    log(f"warmup {args.warmup} ...")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # whole-step wall clock, K steps back to back
+    log(f"timing {args.steps} steps ...")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel HIP-event times over the same number of steps
+    for _ in range(args.steps):
+        step(True)
+    kms = {n: acc_ms[n] / args.steps for n in names}
+
+    edges_per_step = Rq * S * k * k
+    value = edges_per_step / (ms_per_step / 1e3)
+
+    lmb, lmf = lm_bytes(T, V, Hd, k), lm_flops(T, V, Hd)
+    eb = edge_bytes(Rq, S, k, R, Hd)
+    qb = qk_bytes(Rq_a * Lq, Hq, Hkv, D)
+    ab, af = attn_work(attn["seq_lens"], Lq, Hq, Hkv, D, attn["window"])
+    lm_tflops = lmf / (kms["lm_topk"] * 1e-3) / 1e12
+    lm_gbs = lmb / (kms["lm_topk"] * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "edge scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/N(0,0.02) bf16, random paged cache)",
+        "config": {
+            "workload": "DFlash2 candidate step: LM-head top-k + candidate edges at 256 requests x 16 steps "
+                        "(vocab 151936, hidden 4096, top_k 16, rank 128, multiplier 0.5, softcap 30), then "
+                        "draft-layer q/k-norm+RoPE+cache write and block attention at 128 requests x 16 "
+                        "queries (32 q / 8 kv heads, head_dim 128, window 2048, context 512..8192)",
+            "requests": Rq, "steps": S, "top_k": k, "vocab": V, "hidden": Hd, "rank": R,
+            "attn_requests": Rq_a, "attn_queries": Lq, "heads": [Hq, Hkv], "head_dim": D,
+            "window": attn["window"],
+        },
+        "roofline": {
+            "kernel": "dflash_lm_topk (tile GEMM + top-k, and its merge)",
+            "bound": "mfma",
+            "achieved": lm_tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": lm_tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": traffic_for("lm_topk_full"),
+        },
+        "kernels": {
+            "lm_topk": {"ms": kms["lm_topk"], "GB_per_s": lm_gbs, "hbm_frac": lm_gbs / HBM_PEAK_GBS,
+                        "TFLOP_per_s": lm_tflops, "mfma_frac": lm_tflops / MFMA_BF16_PEAK_TFLOPS,
+                        "algorithmic_bytes": lmb, "flops": lmf},
+            "edges": {"ms": kms["edges"], "edge_scores_per_s": edges_per_step / (kms["edges"] * 1e-3),
+                      "GB_per_s": eb / (kms["edges"] * 1e-3) / 1e9,
+                      "hbm_frac": eb / (kms["edges"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": eb},
+            "qk_norm_rope_cache": {"ms": kms["qk"], "GB_per_s": qb / (kms["qk"] * 1e-3) / 1e9,
+                                   "hbm_frac": qb / (kms["qk"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   "algorithmic_bytes": qb},
+            "block_attn": {"ms": kms["attn"], "GB_per_s": ab / (kms["attn"] * 1e-3) / 1e9,
+                           "hbm_frac": ab / (kms["attn"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "TFLOP_per_s": af / (kms["attn"] * 1e-3) / 1e12, "algorithmic_bytes": ab,
+                           "flops": af},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(cand, attn, edges_per_step, 128)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+"""Python binding of libdflash.so, the DFlash2 block-draft candidate step on
+MI355X (gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels behind the
+C ABI of ``include/dflash.h``.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DFlashError", "lib", "lm_topk", "lm_topk_workspace_size", "candidate_edges",
+    "candidate_edges_workspace_size", "rope_cos_sin", "qk_norm_rope_cache", "block_attn",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
+
+_c_i32, _c_i64, _c_f32, _c_f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+_c_p, _c_sz = ctypes.c_void_p, ctypes.c_size_t
+
+_SIGS = {
+    "dflash_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dflash_version": (ctypes.c_int, []),
+    "dflash_lm_topk_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32]),
+    "dflash_lm_topk": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32,
+                                      _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "dflash_candidate_edges_workspace_size": (_c_sz, [_c_i64, _c_i32, _c_i64]),
+    "dflash_candidate_edges": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32,
+                                              _c_i32, _c_i64, _c_i32, _c_i64, _c_p, _c_p, _c_sz, _c_p]),
+    "dflash_rope_cos_sin": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_f64, _c_p]),
+    "dflash_qk_norm_rope_cache": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
+                                                 _c_f32, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32,
+                                                 _c_p, _c_p, _c_p]),
+    "dflash_block_attn_workspace_size": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
+    "dflash_block_attn": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i64, _c_i32, _c_i32,
+                                         _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_sz, _c_p]),
+}
+
+_LIB = None
+
+
+class DFlashError(RuntimeError):
+    """A libdflash call returned a non-OK status."""
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdflash.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise DFlashError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_draft_candidate_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().dflash_status_string(status).decode()
+        raise DFlashError(f"{what}: status {status} ({msg})")
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _workspace(nbytes: int, device, ws):
+    if ws is None:
+        return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    return ws
+
+
+# ---------------------------------------------------------------- LM-head top-k
+def lm_topk_workspace_size(T: int, V: int, Hd: int, k: int) -> int:
+    return int(lib().dflash_lm_topk_workspace_size(T, V, Hd, k))
+
+
+def lm_topk(H: torch.Tensor, W: torch.Tensor, k: int, output_multiplier: float = 1.0,
+            softcap: float = 0.0, ids: torch.Tensor | None = None,
+            logits: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+            stream=None):
+    """Top-k token ids and logits of ``H [T, Hd]`` (bf16) under the LM head
+    ``W [V, Hd]`` (bf16).  Returns ``(ids int32 [T, k], logits fp32 [T, k])``."""
+    T, Hd = H.shape
+    V = W.shape[0]
+    if W.shape[1] != Hd:
+        raise ValueError("H and W disagree on the hidden size")
+    dev = H.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    logits = torch.empty((T, k), dtype=torch.float32, device=dev) if logits is None else logits
+    ws = _workspace(lm_topk_workspace_size(T, V, Hd, k), dev, workspace)
+    st = lib().dflash_lm_topk(_dev(H, torch.bfloat16, "H"), _dev(W, torch.bfloat16, "W"), T, V, Hd, k,
+                              float(output_multiplier), float(softcap),
+                              _dev(ids, torch.int32, "ids"), _dev(logits, torch.float32, "logits"),
+                              ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dflash_lm_topk")
+    return ids, logits
+
+
+# ---------------------------------------------------------------- edge scores
+def candidate_edges_workspace_size(T: int, R: int, Hd: int) -> int:
+    return int(lib().dflash_candidate_edges_workspace_size(T, R, Hd))
+
+
+def candidate_edges(pred_cb, succ_cb, cand_ids, unary, H, W_proj, anchor,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Edge scores ``[Rq, S, k, k]`` (fp32) of the candidate selector."""
+    Rq, S, k = cand_ids.shape
+    V, R = pred_cb.shape
+    Hd = H.shape[1]
+    if succ_cb.shape != (V, R) or W_proj.shape != (R, Hd) or H.shape[0] != Rq * S:
+        raise ValueError("shape mismatch between codebooks, projection and hidden states")
+    if unary.shape != (Rq, S, k) or anchor.shape != (Rq,):
+        raise ValueError("unary must be [Rq, S, k] and anchor [Rq]")
+    dev = H.device
+    out = torch.empty((Rq, S, k, k), dtype=torch.float32, device=dev) if out is None else out
+    ws = _workspace(candidate_edges_workspace_size(Rq * S, R, Hd), dev, workspace)
+    st = lib().dflash_candidate_edges(
+        _dev(pred_cb, torch.bfloat16, "pred_cb"), _dev(succ_cb, torch.bfloat16, "succ_cb"),
+        _dev(cand_ids, torch.int32, "cand_ids"), _dev(unary, torch.float32, "unary"),
+        _dev(H, torch.bfloat16, "H"), _dev(W_proj, torch.bfloat16, "W_proj"),
+        _dev(anchor, torch.int32, "anchor"), Rq, S, k, V, R, Hd,
+        _dev(out, torch.float32, "out"), ws.data_ptr(), ws.numel() * ws.element_size(),
+        _stream(stream))
+    _check(st, "dflash_candidate_edges")
+    return out
+
+
+# ---------------------------------------------------------------- q/k norm, RoPE, cache
+def rope_cos_sin(max_pos: int, D: int, theta: float, device, out=None, stream=None) -> torch.Tensor:
+    """fp32 ``[max_pos, D]`` table: cos in ``[:, :D/2]``, sin in ``[:, D/2:]``."""
+    out = torch.empty((max_pos, D), dtype=torch.float32, device=device) if out is None else out
+    _check(lib().dflash_rope_cos_sin(_dev(out, torch.float32, "cos_sin"), max_pos, D, float(theta),
+                                     _stream(stream)), "dflash_rope_cos_sin")
+    return out
+
+
+def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, positions, cos_sin,
+                       slots=None, kv_cache=None, q_out=None, k_out=None, want_k: bool = True,
+                       stream=None):
+    """Fused per-head RMSNorm + NeoX RoPE of the q and k heads of ``qkv``
+    ``[T, >= (Hq + 2 Hkv) D]`` (bf16), writing K/V into ``kv_cache`` at
+    ``slots`` when both are given.  Returns ``(q_out, k_out or None)``."""
+    T = qkv.shape[0]
+    if qkv.dim() != 2 or qkv.stride(1) != 1:
+        raise ValueError("qkv must be 2-D with unit column stride")
+    dev = qkv.device
+    q_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if q_out is None else q_out
+    if want_k and k_out is None:
+        k_out = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    if (slots is None) != (kv_cache is None):
+        raise ValueError("slots and kv_cache go together")
+    nblk, bs = (kv_cache.shape[0], kv_cache.shape[2]) if kv_cache is not None else (0, 0)
+    if kv_cache is not None and (kv_cache.dim() != 4 or kv_cache.shape[1] != Hkv or kv_cache.shape[3] != 2 * D):
+        raise ValueError("kv_cache must be [num_blocks, Hkv, block_size, 2D]")
+    if qkv.dtype != torch.bfloat16 or not qkv.is_cuda:
+        raise TypeError("qkv must be a bf16 device tensor")
+    st = lib().dflash_qk_norm_rope_cache(
+        qkv.data_ptr(), qkv.stride(0), T, Hq, Hkv, D, _dev(q_w, torch.bfloat16, "q_w"),
+        _dev(k_w, torch.bfloat16, "k_w"), float(eps), _dev(positions, torch.int64, "positions"),
+        _dev(cos_sin, torch.float32, "cos_sin"), cos_sin.shape[0],
+        None if slots is None else _dev(slots, torch.int64, "slots"),
+        None if kv_cache is None else _dev(kv_cache, torch.bfloat16, "kv_cache"), nblk, bs,
+        _dev(q_out, torch.bfloat16, "q_out"), None if k_out is None else _dev(k_out, torch.bfloat16, "k_out"),
+        _stream(stream))
+    _check(st, "dflash_qk_norm_rope_cache")
+    return q_out, k_out
+
+
+# ---------------------------------------------------------------- block attention
+def block_attn(q, kv_cache, block_tables, seq_lens, Lq: int, window: int, scale: float | None = None,
+               out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Non-causal sliding-window attention of each request's ``Lq`` queries
+    ``q [Rq*Lq, Hq, D]`` over the paged cache ``[num_blocks, Hkv, bs, 2D]``."""
+    TQ, Hq, D = q.shape
+    nblk, Hkv, bs, D2 = kv_cache.shape
+    if D2 != 2 * D:
+        raise ValueError("kv_cache last dim must be 2 * head_dim")
+    Rq = seq_lens.shape[0]
+    if TQ != Rq * Lq:
+        raise ValueError("q must hold Lq queries per request")
+    scale = D ** -0.5 if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    ws = _workspace(int(lib().dflash_block_attn_workspace_size(Rq, Lq, Hq, D)), q.device, workspace)
+    st = lib().dflash_block_attn(
+        _dev(q, torch.bfloat16, "q"), _dev(kv_cache, torch.bfloat16, "kv_cache"), nblk,
+        _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, torch.int32, "seq_lens"), Rq, Lq, Hq, Hkv, D, bs, int(window), float(scale),
+        _dev(out, torch.bfloat16, "out"), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dflash_block_attn")
+    return out

@@ -1,0 +1,142 @@
+// Draft-layer q/k RMSNorm + NeoX RoPE + slot-mapped K/V cache write, one pass
+// (DFlash2BeamAttention.forward calls beam_qk_norm_rope with q_norm/k_norm
+// weights, the rope's cos/sin cache and, when the cache is bf16, the layer's
+// kv cache and slot mapping).
+//
+// Sixteen lanes own one head (head_dim 128 = 16 lanes x 8 bf16, one 16-byte
+// load and store per lane); a 256-thread workgroup handles 16 heads.  The sum of
+// squares is reduced inside the 16-lane group, and the RoPE partner (i <-> i +
+// 64) of a lane's 8 elements lives in lane ^ 8 of the same group.  V heads are
+// copied to the cache bit for bit.
+#include "common.h"
+
+namespace dflash {
+
+constexpr int QK_D = 128;
+
+__global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
+    const uint16_t* __restrict__ qkv, int64_t row_stride, int64_t n_items, int Hq, int Hkv,
+    const uint16_t* __restrict__ q_w, const uint16_t* __restrict__ k_w, float eps,
+    const int64_t* __restrict__ positions, const float* __restrict__ cos_sin, int64_t max_pos,
+    const int64_t* __restrict__ slots, uint16_t* __restrict__ cache, int64_t num_blocks, int block_size,
+    uint16_t* __restrict__ q_out, uint16_t* __restrict__ k_out) {
+    const int NH = Hq + 2 * Hkv;
+    const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (item >= n_items) return;
+    const int64_t t = item / NH;
+    const int h = (int)(item - t * NH);
+    const int j = threadIdx.x & 15;
+
+    const u32x4 raw = ldg16(qkv + t * row_stride + (int64_t)h * QK_D + j * 8);
+
+    int64_t cache_row = -1;  // element offset of [blk, head, off, 0] in the cache
+    if (cache != nullptr && h >= Hq) {
+        const int64_t s = slots[t];
+        if (s >= 0 && s < num_blocks * block_size) {
+            const int64_t blk = s / block_size, off = s - blk * block_size;
+            const int hk = (h >= Hq + Hkv) ? h - Hq - Hkv : h - Hq;
+            cache_row = ((blk * Hkv + hk) * block_size + off) * (2 * QK_D);
+        }
+    }
+    if (h >= Hq + Hkv) {  // v head: copied as is
+        if (cache_row >= 0) stg16(cache + cache_row + QK_D + j * 8, raw);
+        return;
+    }
+
+    float x[8];
+    unpack8(raw, x);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 16);
+    const float rinv = 1.0f / sqrtf(ss * (1.0f / QK_D) + eps);
+
+    const bool is_q = h < Hq;
+    float w[8];
+    unpack8(ldg16((is_q ? q_w : k_w) + j * 8), w);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * rinv * w[e];
+
+    int64_t pos = positions[t];
+    pos = pos < 0 ? 0 : (pos >= max_pos ? max_pos - 1 : pos);
+    const float* cs = cos_sin + pos * QK_D + (j & 7) * 8;
+    const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
+    const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + QK_D / 2);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + QK_D / 2 + 4);
+    const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float partner = __shfl_xor(y[e], 8, 16);
+        // first half: x1 cos - x2 sin;  second half: x2 cos + x1 sin
+        o[e] = (j < 8) ? (y[e] * cv[e] - partner * sv[e]) : (y[e] * cv[e] + partner * sv[e]);
+    }
+    u32x4 packed;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) packed[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+
+    if (is_q) {
+        stg16(q_out + (t * Hq + h) * QK_D + j * 8, packed);
+    } else {
+        const int hk = h - Hq;
+        if (k_out != nullptr) stg16(k_out + (t * Hkv + hk) * QK_D + j * 8, packed);
+        if (cache_row >= 0) stg16(cache + cache_row + j * 8, packed);
+    }
+}
+
+// cos_sin[p, i] = cos(p * theta^(-2i/D)), cos_sin[p, D/2 + i] = sin(...), in fp64.
+__global__ void rope_cos_sin_kernel(float* __restrict__ out, int64_t max_pos, int D, double theta) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int half = D / 2;
+    if (idx >= max_pos * half) return;
+    const int64_t p = idx / half;
+    const int i = (int)(idx - p * half);
+    const double inv_freq = pow(theta, -2.0 * (double)i / (double)D);
+    const double ang = (double)p * inv_freq;
+    out[p * D + i] = (float)cos(ang);
+    out[p * D + half + i] = (float)sin(ang);
+}
+
+}  // namespace dflash
+
+using namespace dflash;
+
+extern "C" int dflash_rope_cos_sin(float* cos_sin, int64_t max_pos, int32_t D, double theta, void* stream) {
+    if (!cos_sin || max_pos < 1 || D < 2 || (D & 1) || !(theta > 0.0)) return DFLASH_ERR_INVALID_ARG;
+    if (max_pos > ((int64_t)1 << 40) / D) return DFLASH_ERR_UNSUPPORTED;
+    const int64_t n = max_pos * (D / 2);
+    hipLaunchKernelGGL(rope_cos_sin_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), cos_sin, max_pos, (int)D, theta);
+    DFLASH_LAUNCH_CHECK();
+    return DFLASH_OK;
+}
+
+extern "C" int dflash_qk_norm_rope_cache(const uint16_t* qkv, int64_t row_stride, int64_t T_q, int32_t Hq,
+                                         int32_t Hkv, int32_t D, const uint16_t* q_w, const uint16_t* k_w,
+                                         float eps, const int64_t* positions, const float* cos_sin,
+                                         int64_t max_pos, const int64_t* slots, uint16_t* kv_cache,
+                                         int64_t num_blocks, int32_t block_size, uint16_t* q_out,
+                                         uint16_t* k_out, void* stream) {
+    const void* req[] = {qkv, q_w, k_w, positions, cos_sin, q_out};
+    for (const void* q : req)
+        if (!q || !DFLASH_ALIGNED16(q)) return DFLASH_ERR_INVALID_ARG;
+    if ((slots == nullptr) != (kv_cache == nullptr)) return DFLASH_ERR_INVALID_ARG;
+    if (kv_cache && (!DFLASH_ALIGNED16(kv_cache) || num_blocks < 1 || block_size < 1))
+        return DFLASH_ERR_INVALID_ARG;
+    if (k_out && !DFLASH_ALIGNED16(k_out)) return DFLASH_ERR_INVALID_ARG;
+    if (!k_out && !kv_cache) return DFLASH_ERR_INVALID_ARG;
+    if (T_q < 1 || Hq < 1 || Hkv < 1 || max_pos < 1 || !(eps >= 0.f)) return DFLASH_ERR_INVALID_ARG;
+    if (D != QK_D) return DFLASH_ERR_UNSUPPORTED;
+    if (row_stride < (int64_t)(Hq + 2 * Hkv) * D || row_stride % 8 != 0) return DFLASH_ERR_INVALID_ARG;
+    const int64_t n_items = T_q * (int64_t)(Hq + 2 * Hkv);
+    if (n_items / 16 + 1 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(qk_norm_rope_cache_kernel, dim3((unsigned)((n_items + 15) / 16)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), qkv, row_stride, n_items, Hq, Hkv, q_w, k_w,
+                       eps, positions, cos_sin, max_pos, slots, kv_cache, num_blocks, block_size, q_out, k_out);
+    DFLASH_LAUNCH_CHECK();
+    return DFLASH_OK;
+}

@@ -251,13 +251,15 @@ def block_attn(q, cache, block_tables, seq_lens, Lq: int, Hq: int, Hkv: int,
         rows = cache[phys, :, kpos % block_size, :]            # [nk, Hkv, 2D]
         Kf = bf16_to_f64(rows[:, :, :D])
         Vf = bf16_to_f64(rows[:, :, D:])
+        visible = np.zeros((Lq, len(kpos)), dtype=bool)       # [query, key]
         for i in range(Lq):
             lo, hi = attention_window(L, Lq, i, window)
-            sel = slice(lo - lo0, hi - lo0)
-            for h in range(Hq):
-                kh = h // group
-                s = Kf[sel, kh, :] @ qf[r, i, h] * scale
-                p = np.exp(s - s.max())
-                p /= p.sum()
-                out[r, i, h] = p @ Vf[sel, kh, :]
+            visible[i] = (kpos >= lo) & (kpos < hi)
+        for kh in range(Hkv):
+            Q = qf[r, :, kh * group:(kh + 1) * group, :]       # [Lq, group, D]
+            s = np.einsum("igd,jd->igj", Q, Kf[:, kh, :]) * scale
+            s = np.where(visible[:, None, :], s, -np.inf)
+            p = np.exp(s - s.max(axis=-1, keepdims=True))
+            p /= p.sum(axis=-1, keepdims=True)
+            out[r, :, kh * group:(kh + 1) * group, :] = p @ Vf[:, kh, :]
     return f64_to_bf16(out.reshape(Rq * Lq, Hq, D))

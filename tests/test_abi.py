@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: libdflash.so loads, exports every entry point that
+include/dflash.h declares, and rejects bad arguments on the host before any
+launch (the error paths a test can force from the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import block_draft_candidate_amd as B
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libdflash.so not built")
+    return B.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(5):
+        assert L.dflash_status_string(code)
+    assert L.dflash_status_string(99) == b"unknown status"
+    assert L.dflash_version() >= 100
+
+
+FAKE = 1 << 20  # an aligned, never dereferenced address: only host checks run
+
+
+@pytest.fixture(autouse=True)
+def _no_gpu_for_fake_pointers(request):
+    # The validation tests pass fake device addresses; they must never reach a
+    # real launch, so they run only where no GPU is visible.
+    if "validation" in request.node.name:
+        import torch
+        if torch.cuda.device_count() > 0:
+            pytest.skip("fake-pointer validation tests run on a host without a GPU")
+
+
+def test_lm_topk_host_validation(L):
+    f = L.dflash_lm_topk
+    ok = dict(H=FAKE, W=FAKE, T=8, V=1024, Hd=256, k=4, s=1.0, c=0.0, ids=FAKE, lg=FAKE, ws=FAKE)
+    ws = L.dflash_lm_topk_workspace_size(8, 1024, 256, 4)
+    assert ws > 0
+
+    def call(**o):
+        a = dict(ok, **o)
+        return f(a["H"], a["W"], a["T"], a["V"], a["Hd"], a["k"], a["s"], a["c"], a["ids"], a["lg"],
+                 a["ws"], a.get("wsb", 0), None)
+
+    assert call(H=None, wsb=ws) == 1
+    assert call(H=FAKE + 2, wsb=ws) == 1          # misaligned
+    assert call(k=0, wsb=ws) == 1
+    assert call(k=2000, wsb=ws) == 1              # k > V
+    assert call(s=0.0, wsb=ws) == 1               # multiplier must be > 0
+    assert call(s=float("inf"), wsb=ws) == 1
+    assert call(c=float("nan"), wsb=ws) == 1
+    assert call(k=65, V=4096, wsb=ws) == 2        # k > 64 unsupported
+    assert call(Hd=260, wsb=ws) == 2              # Hd % 8
+    assert call(wsb=ws - 1) == 3                  # workspace too small
+    assert L.dflash_lm_topk_workspace_size(0, 1, 1, 1) == 0
+
+
+def test_edges_host_validation(L):
+    f = L.dflash_candidate_edges
+    ws = L.dflash_candidate_edges_workspace_size(8, 16, 256)
+    assert ws > 0
+
+    def call(**o):
+        a = dict(Rq=2, S=4, k=4, V=1024, R=16, Hd=256, wsb=ws, anchor=FAKE)
+        a.update(o)
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["anchor"], a["Rq"], a["S"], a["k"], a["V"], a["R"],
+                 a["Hd"], FAKE, FAKE, a["wsb"], None)
+
+    assert call(anchor=None) == 1
+    assert call(k=0) == 1
+    assert call(R=24) == 2          # R % 16
+    assert call(R=512) == 2         # R > 256 in this build
+    assert call(k=65, V=4096) == 2
+    assert call(wsb=ws - 4) == 3
+
+
+def test_qk_host_validation(L):
+    f = L.dflash_qk_norm_rope_cache
+
+    def call(slots=FAKE, cache=FAKE, kout=FAKE, D=128, stride=24 * 128, eps=1e-6):
+        return f(FAKE, stride, 288, 16, 4, D, FAKE, FAKE, eps, FAKE, FAKE, 4096, slots, cache, 256, 16,
+                 FAKE, kout, None)
+
+    assert call(slots=None) == 1            # exactly one of slots / cache
+    assert call(slots=None, cache=None, kout=None) == 1  # nothing to write K to
+    assert call(D=64) == 2
+    assert call(stride=100) == 1
+    assert call(eps=-1.0) == 1
+    assert L.dflash_rope_cos_sin(None, 10, 128, 1e6, None) == 1
+    assert L.dflash_rope_cos_sin(FAKE, 10, 127, 1e6, None) == 1
+
+
+def test_attn_host_validation(L):
+    f = L.dflash_block_attn
+
+    def call(Lq=16, Hq=32, Hkv=8, D=128, bs=16, window=2048, scale=0.088):
+        return f(FAKE, FAKE, 100, FAKE, 10, FAKE, 4, Lq, Hq, Hkv, D, bs, window, scale, FAKE, None, 0, None)
+
+    assert call(Hq=30) == 1          # Hq % Hkv
+    assert call(window=0) == 1
+    assert call(scale=0.0) == 1
+    assert call(Lq=17) == 2
+    assert call(D=64) == 2
+    assert call(bs=32) == 2
+    assert call(Hq=24, Hkv=2) == 2   # group of 12 heads
+    assert L.dflash_block_attn_workspace_size(4, 16, 32, 128) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import block_draft_candidate_amd as B
+    monkeypatch.setattr(B, "_LIB", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(B.DFlashError):
+        B.lib()

@@ -1,0 +1,87 @@
+"""GPU parity of dflash_candidate_edges against the oracle
+(DFlash2BeamCandidateSelector edge scores [requests, steps, top_k, top_k])."""
+import numpy as np
+import pytest
+
+from oracle import dflash_oracle as O
+import workloads as WL
+from tests.parity import check_edges
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_draft_candidate_amd as B
+    B.lib()
+    return B
+
+
+def _gpu_edges(B, d):
+    from tests.gpu_common import dev, dev_bf16
+    E = B.candidate_edges(dev_bf16(d["P"]), dev_bf16(d["S"]), dev(d["ids"]), dev(d["U"]),
+                          dev_bf16(d["H"]), dev_bf16(d["Wp"]), dev(d["anchor"]))
+    return E.cpu().numpy()
+
+
+def _ref(d):
+    return O.candidate_edges(d["P"], d["S"], d["ids"], d["U"], d["H"], d["Wp"], d["anchor"])
+
+
+def _amplified(d, seed):
+    """Codebooks drawn N(0, 1) so the bilinear term dominates the unary logit."""
+    V, R = d["P"].shape
+    e = dict(d)
+    e["P"] = WL.bf16_normal(seed, 20, (V, R))
+    e["S"] = WL.bf16_normal(seed, 21, (V, R))
+    return e
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "full"])
+def test_workload_all_rows(B, name):
+    from tests.gpu_common import candidate, say
+    d = candidate(name) if name == "full" else WL.candidate_inputs(name)
+    E = _gpu_edges(B, d)
+    check_edges(E, _ref(d), d["U"], name)
+    a = _amplified(d, 700 + len(name))
+    Ea = _gpu_edges(B, a)
+    check_edges(Ea, _ref(a), a["U"], name + " amplified")
+    say(f"[edges {name}] max|dE|={np.abs(E - _ref(d)).max():.3g}")
+
+
+def test_large_workload_subset(B):
+    d = WL.candidate_inputs("large", requests=96)
+    E = _gpu_edges(B, d)
+    check_edges(E, _ref(d), d["U"], "large")
+
+
+@pytest.mark.parametrize("Rq,S,k,V,R,Hd", [
+    (3, 5, 3, 100, 16, 24),       # k < 16, R = 16 (4-wide lane chunks), Hd % 64 != 0
+    (5, 2, 20, 300, 48, 520),     # k in (16, 32], R % 32 != 0
+    (2, 3, 40, 500, 256, 64),     # k in (32, 64], R = 256
+    (1, 1, 1, 10, 32, 8),         # one request, one step, k = 1
+    (77, 3, 16, 2000, 128, 4104), # ragged row count for the projection tiles
+])
+def test_shapes(B, Rq, S, k, V, R, Hd):
+    rng = np.random.default_rng(Rq * 1000 + k)
+    bf = lambda shape, s: WL.to_bf16_bits((rng.standard_normal(shape) * s).astype(np.float32))
+    d = dict(P=bf((V, R), 0.5), S=bf((V, R), 0.5), H=bf((Rq * S, Hd), 1.0), Wp=bf((R, Hd), 0.1),
+             ids=np.stack([rng.choice(V, k, replace=False) for _ in range(Rq * S)]).reshape(Rq, S, k).astype(np.int32),
+             U=rng.standard_normal((Rq, S, k)).astype(np.float32),
+             anchor=rng.integers(0, V, Rq).astype(np.int32))
+    check_edges(_gpu_edges(B, d), _ref(d), d["U"], f"shape {Rq, S, k, V, R, Hd}")
+
+
+def test_zero_codebooks_give_unary(B):
+    d = WL.candidate_inputs("mid")
+    d = dict(d, P=np.zeros_like(d["P"]))
+    E = _gpu_edges(B, d)
+    assert np.array_equal(E, np.broadcast_to(d["U"][:, :, None, :], E.shape))
+
+
+def test_deterministic(B):
+    d = WL.candidate_inputs("mid")
+    assert np.array_equal(_gpu_edges(B, d).view(np.uint32), _gpu_edges(B, d).view(np.uint32))

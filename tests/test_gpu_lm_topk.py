@@ -1,0 +1,104 @@
+"""GPU parity of dflash_lm_topk against the oracle (compute_candidates of the
+DFlash2 drafter: LM head, output multiplier, soft cap, per-position top-k)."""
+import numpy as np
+import pytest
+
+from oracle import dflash_oracle as O
+import workloads as WL
+from tests.parity import check_topk_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_draft_candidate_amd as B
+    B.lib()
+    return B
+
+
+def _run(B, H, W, k, s, c):
+    from tests.gpu_common import dev_bf16
+    ids, vals = B.lm_topk(dev_bf16(H), dev_bf16(W), k, s, c)
+    return ids.cpu().numpy(), vals.cpu().numpy()
+
+
+def _check(B, H, W, k, s, c, rows=None, label=""):
+    from tests.gpu_common import say
+    gids, gvals = _run(B, H, W, k, s, c)
+    rows = np.arange(H.shape[0]) if rows is None else np.asarray(rows)
+    keys = O.lm_logit_keys(H, W, s, c, rows=rows)
+    rids, rvals = O.topk_from_keys(keys, k)
+    exact, near = check_topk_rows(gids[rows], gvals[rows], keys, rids, rvals, k)
+    say(f"[lm_topk {label}] rows={len(rows)} exact={exact} near={near}")
+    return gids, gvals
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_small_workloads_all_rows(B, name):
+    d = WL.candidate_inputs(name)
+    _check(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"], label=name)
+
+
+def _random_case(seed, T, V, Hd, sigma_w):
+    rng = np.random.default_rng(seed)
+    H = WL.to_bf16_bits(rng.standard_normal((T, Hd), dtype=np.float32))
+    W = WL.to_bf16_bits(rng.standard_normal((V, Hd), dtype=np.float32) * np.float32(sigma_w))
+    return H, W
+
+
+@pytest.mark.parametrize("T,V,Hd,k,s,c", [
+    (300, 5000, 200, 7, 0.75, 5.0),     # ragged in every dimension, cap well inside tanh's bend
+    (1, 777, 8, 1, 1.0, 0.0),           # one row, k = 1, a single K chunk
+    (37, 4099, 72, 64, 2.0, 30.0),      # k = 64, V just past a tile
+    (513, 20000, 136, 16, 0.5, 30.0),   # three row tiles, two partial
+])
+def test_ragged_shapes(B, T, V, Hd, k, s, c):
+    H, W = _random_case(T * 7 + V, T, V, Hd, 0.2)
+    _check(B, H, W, k, s, c, label=f"T{T} V{V} Hd{Hd} k{k}")
+
+
+def test_one_hot_exact_at_full_vocab(B):
+    """One-hot hidden states make every logit an LM-head weight exactly on both
+    sides, so all ids must match the oracle bit for bit."""
+    d = WL.candidate_inputs("full", requests=4)
+    W = d["W"]
+    T, Hd = 64, W.shape[1]
+    rng = np.random.default_rng(9)
+    H = np.zeros((T, Hd), np.uint16)
+    H[np.arange(T), rng.integers(0, Hd, T)] = 0x3F80
+    k = d["top_k"]
+    gids, gvals = _run(B, H, W, k, 1.0, 0.0)
+    keys = O.lm_logit_keys(H, W, 1.0, 0.0)
+    rids, rvals = O.topk_from_keys(keys, k)
+    assert np.array_equal(gids, rids)
+    assert np.array_equal(gvals, rvals)
+    # a power-of-two multiplier keeps the logits exact as well
+    gids, gvals = _run(B, H, W, k, 0.5, 0.0)
+    rids, rvals = O.topk_from_keys(O.lm_logit_keys(H, W, 0.5, 0.0), k)
+    assert np.array_equal(gids, rids) and np.array_equal(gvals, rvals)
+
+
+def test_full_workload_sampled_rows(B):
+    """The 256 x 16 workload in the launch configuration the benchmark times;
+    the oracle checks rows spread over every 256-row tile."""
+    from tests.gpu_common import candidate
+    d = candidate("full")
+    T = d["H"].shape[0]
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, T - 1], rng.integers(0, T, 27)]))
+    gids, gvals = _check(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"], rows, "full")
+    # deterministic: a second call gives the same bits
+    gids2, gvals2 = _run(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"])
+    assert np.array_equal(gids, gids2) and np.array_equal(gvals.view(np.uint32), gvals2.view(np.uint32))
+
+
+def test_large_vocab_tie_heavy_sampled_rows(B):
+    d = WL.candidate_inputs("large", requests=64)
+    T = d["H"].shape[0]
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 14)]))
+    _check(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"], rows, "large")
