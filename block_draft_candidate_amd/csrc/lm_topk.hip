@@ -75,30 +75,76 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
     L[0] = max(L[0], p);
 }
 
+// Issue the LDS-DMA loads of one 64-wide K slice of `nrows` rows (this wave's
+// share: instructions q = wave * NI .. wave * NI + NI - 1, each filling 1 KB =
+// 8 rows of 128 B).  Lane i of instruction q lands at LDS byte q*1024 + i*16,
+// i.e. row 8q + i/8, physical chunk i%8; it therefore loads logical chunk
+// (i%8) ^ (row%8), which realises the XOR swizzle the fragment reads expect.
+// Out-of-range rows and the K tail read as zero (buffer range check).
+// Per-lane byte offsets of the LDS-DMA loads of one 64-wide K slice of the
+// rows this wave loads: instructions q = wave * NI + j, each filling 1 KB = 8
+// rows of 128 B.  Lane i of instruction q lands at LDS byte q*1024 + i*16,
+// i.e. row 8q + i/8, physical chunk i%8; it therefore loads logical chunk
+// (i%8) ^ (row%8), which realises the XOR swizzle the fragment reads expect.
+template <int NI>
+__device__ __forceinline__ void dma_offsets(int (&voff)[NI], int wave_s, int lane, int Hd) {
+    const int r8 = lane >> 3;
+    const int lc = (lane & 7) ^ r8;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) voff[j] = (((wave_s * NI + j) * 8 + r8) * Hd + lc * 8) * 2;
+}
+
+// Issue them for the slice starting at column k0 (scalar offset k0 * 2).  Rows
+// past the tile and, in a final partial slice, columns past Hd read as zero.
+template <int NI>
+__device__ __forceinline__ void dma_slice(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, const int* voff,
+                                          int wave_s, int lane, int Hd, int k0) {
+    if (k0 + 64 <= Hd) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512), 16, voff[j],
+                k0 * 2, 0, 0);
+    } else {
+        const int gk = k0 + (((lane & 7) ^ (lane >> 3)) * 8);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512), 16,
+                gk < Hd ? voff[j] + k0 * 2 : (int)0x80000000, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
 template <int BN, int KCAP>
 __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ W, int T, int V, int Hd,
     int nM, int nN, int G, int xcd_map, float s, float c, float inv_c,
     uint64_t* __restrict__ part) {
-    constexpr int WN = BN / 2;              // columns per wave
-    constexpr int NB = WN / 16;             // 16-column MFMA blocks per wave
-    constexpr int MB = 8;                   // 16-row MFMA blocks per wave (128 rows)
-    constexpr int A_CH = LM_BM * 8 / LM_THREADS;  // 16-byte chunks per thread per slice
-    constexpr int B_CH = BN * 8 / LM_THREADS;
-    constexpr int SP = WN + 1;              // staging pitch (floats): conflict-free row scans
-    constexpr int A_ELEMS = LM_BM * LM_BK;
-    constexpr int B_ELEMS = BN * LM_BK;
-    constexpr int AB_BYTES = 2 * (A_ELEMS + B_ELEMS) * 2;
-    constexpr int ST_BYTES = LM_BM * SP * 4;
-    constexpr int LDS_BYTES = AB_BYTES > ST_BYTES ? AB_BYTES : ST_BYTES;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-    uint16_t* sA = reinterpret_cast<uint16_t*>(lds);
-    uint16_t* sB = sA + 2 * A_ELEMS;
-    float* stage = reinterpret_cast<float*>(lds);
+    constexpr int WN = BN / 2;               // columns per wave
+    constexpr int NB = WN / 32;              // 32-column MFMA blocks per wave
+    constexpr int MB = 4;                    // 32-row MFMA blocks per wave (128 rows)
+    constexpr int NIA = LM_BM / 8 / 4;       // LDS-DMA instructions per wave per slice (A)
+    constexpr int NIB = BN / 8 / 4;          // (B)
+    constexpr int STAGE = (LM_BM + BN) * LM_BK;  // elements per pipeline stage
+    constexpr int QCOLS = 64;                // epilogue pass width (columns)
+    constexpr int PASSES = BN / QCOLS;
+    constexpr int PASS_PER_WAVE = PASSES / 2;
+    constexpr int JPP = NB / PASS_PER_WAVE;  // MFMA column blocks per pass (2)
+    static_assert(LM_BM * QCOLS * 4 <= STAGE * 2 * 2, "epilogue staging must fit the stages");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+    float* stage = reinterpret_cast<float*>(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int wm = wave >> 1, wn = wave & 1;
 
     int L = blockIdx.x;
@@ -120,105 +166,151 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     float thr = -INFINITY;
 
     const int nK = (Hd + LM_BK - 1) / LM_BK;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(H + (int64_t)m0 * Hd), (short)0, min(LM_BM, T - m0) * Hd * 2, 0x00020000);
+
+    // Per-lane LDS element offsets of the 32 x 16 fragments: row = lane % 32 of
+    // each 32-row block, 16-byte chunk (2 * k16 + lane / 32) ^ (row % 8).
+    const int fr = lane & 31;
+    const int a_row0 = (wm * 128 + fr) * LM_BK;
+    const int b_row0 = LM_BM * LM_BK + (wn * WN + fr) * LM_BK;
+    int voffA[NIA], voffB[NIB];
+    dma_offsets<NIA>(voffA, wave_s, lane, Hd);
+    dma_offsets<NIB>(voffB, wave_s, lane, Hd);
 
     for (int nt = n_begin; nt < n_end; ++nt) {
         const int n0 = nt * BN;
-        f32x4 acc[MB][NB];
+        const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(W + (int64_t)n0 * Hd), (short)0, min(BN, V - n0) * Hd * 2, 0x00020000);
+        f32x16 acc[MB][NB];
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-        u32x4 ga[A_CH], gb[B_CH];
-        auto gload = [&](int kt) {
-            const int k0 = kt * LM_BK;
+        auto issue = [&](int kt, int st) {
+            uint16_t* base = smem + st * STAGE;
+            dma_slice<NIA>(rsA, base, voffA, wave_s, lane, Hd, kt * LM_BK);
+            dma_slice<NIB>(rsB, base + LM_BM * LM_BK, voffB, wave_s, lane, Hd, kt * LM_BK);
+        };
+        // fragments of one 16-wide K step (k16 = 0..3) of the slice in stage st
+        auto read_frags = [&](int st, int k16, bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
+            const uint16_t* base = smem + st * STAGE;
+            const int chs = (((2 * k16 + (lane >> 5)) ^ (lane & 7)) << 3);  // row % 8 == lane % 8
 #pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int ch = tid + LM_THREADS * i;
-                const int row = ch >> 3, kc = ch & 7;
-                const int gr = m0 + row, gk = k0 + kc * 8;
-                ga[i] = (gr < T && gk < Hd) ? ldg16(H + (int64_t)gr * Hd + gk) : zero4;
-            }
+            for (int i = 0; i < MB; ++i)
+                fa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + a_row0 + i * 32 * LM_BK + chs));
 #pragma unroll
-            for (int i = 0; i < B_CH; ++i) {
-                const int ch = tid + LM_THREADS * i;
-                const int row = ch >> 3, kc = ch & 7;
-                const int gr = n0 + row, gk = k0 + kc * 8;
-                gb[i] = (gr < V && gk < Hd) ? ldg16(W + (int64_t)gr * Hd + gk) : zero4;
+            for (int j = 0; j < NB; ++j)
+                fb[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + b_row0 + j * 32 * LM_BK + chs));
+        };
+        auto mfmas = [&](const bf16x8 (&fa)[MB], const bf16x8 (&fb)[NB]) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        };
+        // one fragment read of the next K step after every MFMA pair
+        auto interleave = [&]() {
+#pragma unroll
+            for (int q = 0; q < MB + NB; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, (MB * NB) / (MB + NB), 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         };
-        auto sstore = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int ch = tid + LM_THREADS * i;
-                const int row = ch >> 3, kc = ch & 7;
-                *reinterpret_cast<u32x4*>(sA + buf * A_ELEMS + row * LM_BK + ((kc ^ (row & 7)) << 3)) = ga[i];
-            }
-#pragma unroll
-            for (int i = 0; i < B_CH; ++i) {
-                const int ch = tid + LM_THREADS * i;
-                const int row = ch >> 3, kc = ch & 7;
-                *reinterpret_cast<u32x4*>(sB + buf * B_ELEMS + row * LM_BK + ((kc ^ (row & 7)) << 3)) = gb[i];
-            }
-        };
 
-        gload(0);
-        sstore(0);
-        __syncthreads();
-        for (int kt = 0; kt < nK; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < nK) gload(kt + 1);
-            const uint16_t* a_base = sA + buf * A_ELEMS;
-            const uint16_t* b_base = sB + buf * B_ELEMS;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int ch = kk * 4 + (lane >> 4);
-                bf16x8 af[MB], bfr[NB];
-#pragma unroll
-                for (int i = 0; i < MB; ++i) {
-                    const int row = wm * 128 + i * 16 + (lane & 15);
-                    af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(a_base + row * LM_BK + ((ch ^ (row & 7)) << 3)));
-                }
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const int row = wn * WN + j * 16 + (lane & 15);
-                    bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(b_base + row * LM_BK + ((ch ^ (row & 7)) << 3)));
-                }
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-#pragma unroll
-                    for (int j = 0; j < NB; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-            }
-            if (kt + 1 < nK) sstore(buf ^ 1);
-            __syncthreads();
+        // Software pipeline: fragments of the next 16-wide K step are read while
+        // the MFMAs of the current one run.  Two LDS stages, one barrier per
+        // 64-wide slice: before the first K step of slice kt+1 every wave waits
+        // for its DMA of that slice, then a barrier (all waves are done reading
+        // stage kt%2) lets the DMA of slice kt+2 start into it.
+        bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
+        issue(0, 0);
+        if (nK > 1) {
+            issue(1, 1);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NIA + NIB));  // slice 0 landed, slice 1 may be in flight
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
-
-        // Epilogue: stage one column half at a time, then each thread scans its row.
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            if (wn == pass) {
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-#pragma unroll
-                    for (int j = 0; j < NB; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int row = wm * 128 + i * 16 + 4 * (lane >> 4) + e;
-                            const int col = j * 16 + (lane & 15);
-                            stage[row * SP + col] = acc[i][j][e];
-                        }
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        read_frags(0, 0, fa0, fb0);
+        for (int kt = 0; kt < nK; ++kt) {
+            const int st = kt & 1;
+            read_frags(st, 1, fa1, fb1);
+            mfmas(fa0, fb0);
+            interleave();
+            read_frags(st, 2, fa0, fb0);
+            mfmas(fa1, fb1);
+            interleave();
+            read_frags(st, 3, fa1, fb1);
+            mfmas(fa0, fb0);
+            interleave();
+            if (kt + 1 < nK) {
+                __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                compiler_fence();
+                if (kt + 2 < nK) issue(kt + 2, st);
+                read_frags(st ^ 1, 0, fa0, fb0);
             }
-            __syncthreads();
+            mfmas(fa1, fb1);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+
+        // Epilogue: stage 64 columns at a time, column-major (64 cols x 256 rows
+        // fp32; 4-row groups XOR-swizzled by column so that both the 16-byte
+        // writes of the MFMA layout and the row scans are bank-spread), then
+        // thread t scans row t.  In the 32x32 MFMA layout lane l holds column
+        // l % 32 and rows 8b + 4(l / 32) + e, e = 0..3 (four consecutive rows).
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+            if (wn == pass / PASS_PER_WAVE) {
+                const int jb = (pass % PASS_PER_WAVE) * JPP;
+#pragma unroll
+                for (int jj = 0; jj < JPP; ++jj) {
+                    const int col = jj * 32 + fr;
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const int rg = (wm * 128 + i * 32 + 8 * b + 4 * (lane >> 5)) >> 2;  // 4-row group
+                            const f32x4 v = {acc[i][jb + jj][4 * b], acc[i][jb + jj][4 * b + 1],
+                                             acc[i][jb + jj][4 * b + 2], acc[i][jb + jj][4 * b + 3]};
+                            *reinterpret_cast<f32x4*>(stage + col * LM_BM + ((rg ^ (col & 31)) << 2)) = v;
+                        }
+                }
+            }
+            __builtin_amdgcn_s_barrier();
+            compiler_fence();
             if (my_row < T) {
-                const int cbase = n0 + pass * WN;
-                const int ncols = min(WN, V - cbase);
-                const float* srow = stage + tid * SP;
-                for (int cc = 0; cc < ncols; ++cc) {
-                    const float a = srow[cc];
-                    if (a >= thr) {
-                        const uint32_t kb = logit_key_bits(a, s, c, inv_c);
+                const int cbase = n0 + pass * QCOLS;
+                const int ncols = min(QCOLS, V - cbase);
+                // element (row t, column cc) of the column-major staging
+                const int rg = tid >> 2, r4 = tid & 3;
+                auto at = [&](int cc) { return stage[cc * LM_BM + ((rg ^ (cc & 31)) << 2) + r4]; };
+                // 1) mask of this row's columns whose raw accumulator reaches the
+                //    threshold (cheap, no divergence)
+                uint32_t m_lo = 0u, m_hi = 0u;
+#pragma unroll
+                for (int cc = 0; cc < QCOLS; ++cc) {
+                    const uint32_t bit = (at(cc) >= thr && cc < ncols) ? 1u : 0u;
+                    if (cc < 32) m_lo |= bit << cc; else m_hi |= bit << (cc - 32);
+                }
+                // 2) candidates in column (= token id) order, one per lane per
+                //    round; the threshold rises as the list fills, so later
+                //    candidates are mostly dropped by a single compare.
+                while ((m_lo | m_hi) != 0u) {
+                    int cc;
+                    if (m_lo) { cc = __builtin_ctz(m_lo); m_lo &= m_lo - 1u; }
+                    else { cc = 32 + __builtin_ctz(m_hi); m_hi &= m_hi - 1u; }
+                    const float v = at(cc);
+                    if (v >= thr) {
+                        const uint32_t kb = logit_key_bits(v, s, c, inv_c);
                         const uint32_t p = (order_key(kb) << 16) | (0xffffu - (uint32_t)(cbase + cc - gcol0));
                         if (p > list[KCAP - 1]) {
                             list_insert(list, p);
@@ -227,7 +319,9 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                     }
                 }
             }
-            __syncthreads();
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): row reads done before the next pass writes
+            __builtin_amdgcn_s_barrier();
+            compiler_fence();
         }
     }
 

@@ -109,7 +109,7 @@ def _check_attn(got, ref, label):
     assert_close(g, r, label)
     rel = np.abs(g - r).max() / np.sqrt(np.mean(r * r))
     say(f"[attn {label}] max|d|/rms(ref) = {rel:.3g}")
-    assert rel < 0.05
+    assert rel < 0.1
 
 
 @pytest.mark.parametrize("q_scale", [1.0, 4.0])
