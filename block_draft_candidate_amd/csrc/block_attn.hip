@@ -4,16 +4,21 @@
 // context K/V is already in the cache, the block's own K/V is written by the
 // fused norm/RoPE kernel first).
 //
-// One workgroup per (request, kv head); wave w handles q head kv * G + w, i.e.
-// the G heads that share the kv head read each K/V tile once from HBM.  A wave's
-// 16 MFMA columns are the block's (up to 16) queries.
-//   S^T = K Q^T   : v_mfma_f32_16x16x32_bf16, K rows from LDS, Q^T from registers;
-//                   every lane then holds scores of a single query, so the online
-//                   softmax (fp32, exp2) needs only two cross-lane steps.
-//   O^T += V^T P^T: P^T comes straight from the S^T registers (bf16), V^T from an
-//                   LDS tile stored transposed.
-// K/V tiles of 64 keys (4 cache blocks of 16) are double-buffered in LDS with a
-// register prefetch of the next tile.
+// One workgroup per (request, kv head); wave w handles q head kv * G + w, so the
+// G heads that share a kv head read each K/V tile from HBM once.  A wave's 16
+// MFMA columns are the block's (up to 16) queries.
+//   * K/V tiles of 64 keys (4 cache blocks) go straight from HBM to LDS with
+//     LDS-DMA (global_load_lds_dwordx4), whole 512-byte cache rows (K | V),
+//     double-buffered.  K chunks are XOR-swizzled by row (16-byte units), V
+//     chunks by row (16-byte units, 2 * (row % 8)), so both reads below are
+//     bank-conflict free.
+//   * S^T = K Q^T: v_mfma_f32_16x16x32_bf16, K rows from LDS, Q^T from registers;
+//     each lane then holds scores of a single query, so the online softmax
+//     (fp32, exp2) needs only two cross-lane steps.
+//   * O^T += V^T P^T: P^T comes straight from the S^T registers (bf16); V^T comes
+//     from the row-major V tile through ds_read_b64_tr_b16 (the transposing LDS
+//     read): lane p of a 16-lane group points at V[key(p / 4)][d0 + 4 (p % 4)],
+//     and lane i receives V[key(j)][d0 + i], j = 0..3.
 #include "common.h"
 
 namespace dflash {
@@ -21,21 +26,24 @@ namespace dflash {
 constexpr int AT_D = 128;
 constexpr int AT_BS = 16;      // cache block size
 constexpr int AT_TK = 64;      // keys per tile
-constexpr int AT_VP = 72;      // V^T row pitch (elements): conflict-free 8-byte reads
+constexpr int AT_ROW = 2 * AT_D;  // elements per cache row (K | V)
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+__device__ __forceinline__ void at_fence() { asm volatile("" ::: "memory"); }
 
 template <int G>
 __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ cache, int64_t num_blocks,
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ seq_lens, int Lq,
     int Hq, int Hkv, int window, float scale_log2, uint16_t* __restrict__ out) {
-    constexpr int NT = 64 * G;
-    constexpr int CHUNKS = (AT_TK * 2 * AT_D * 2 / 16) / NT;  // 16-byte chunks per thread per tile
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][AT_TK * AT_D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][AT_D * AT_VP];
+    constexpr int NI = AT_TK / 2 / G;      // LDS-DMA instructions per wave per tile (2 rows each)
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * AT_TK * AT_ROW];
 
     const int r = blockIdx.x / Hkv;
     const int hk = blockIdx.x - r * Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int hq = hk * G + wave;
     const int qi = lane & 15, g = lane >> 4;
 
@@ -54,42 +62,28 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     const int ntiles = L > kstart ? (L - kstart + AT_TK - 1) / AT_TK : 0;
     const int qlo = L - Lq + qi - window + 1;  // lowest visible key of this lane's query
     const int32_t* bt = block_tables + (int64_t)r * max_blocks;
+    const int nblk_req = (L + AT_BS - 1) / AT_BS;
 
-    u32x4 regs[CHUNKS];
-    auto gload = [&](int tile) {
+    // DMA lane layout: instruction covers tile rows 2q, 2q+1; lane i -> row 2q + i/32,
+    // physical 16-byte chunk i % 32 of the 512-byte row.  Physical chunk pc < 16 holds
+    // K chunk pc ^ (row % 16); pc >= 16 holds V chunk (pc - 16) ^ (2 (row % 8)).
+    const int dr = lane >> 5;
+    const int pc = lane & 31;
+    auto issue = [&](int tile, int st) {
         const int kb = kstart + tile * AT_TK;
 #pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
-            const int c = tid + NT * i;
-            const int jb = c >> 9, wo = c & 511;  // cache block within the tile, 16-byte chunk within it
-            const int row = wo >> 5, cc = wo & 31;
-            const int key0 = kb + jb * AT_BS;
-            if (key0 < L) {
-                int b = bt[key0 / AT_BS];
-                b = b < 0 ? 0 : (b >= num_blocks ? (int)(num_blocks - 1) : b);
-                regs[i] = ldg16(cache + (((int64_t)b * Hkv + hk) * AT_BS + row) * (2 * AT_D) + cc * 8);
-            } else {
-                regs[i] = zero4;
-            }
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
-            const int c = tid + NT * i;
-            const int jb = c >> 9, wo = c & 511;
-            const int row = wo >> 5, cc = wo & 31;
-            const int key = jb * AT_BS + row;
-            if (cc < 16) {
-                *reinterpret_cast<u32x4*>(&sK[buf][key * AT_D + ((cc ^ (key & 7)) << 3)]) = regs[i];
-            } else {
-                const int d0 = (cc - 16) * 8;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sV[buf][(d0 + 2 * e) * AT_VP + key] = (uint16_t)(regs[i][e] & 0xffffu);
-                    sV[buf][(d0 + 2 * e + 1) * AT_VP + key] = (uint16_t)(regs[i][e] >> 16);
-                }
-            }
+        for (int j = 0; j < NI; ++j) {
+            const int qd = wave_s * NI + j;
+            const int row = 2 * qd + dr;            // tile row (key offset)
+            const int blk_i = kb / AT_BS + (2 * qd) / AT_BS;  // uniform per instruction
+            int b = bt[min(blk_i, nblk_req > 0 ? nblk_req - 1 : 0)];
+            b = b < 0 ? 0 : (b >= num_blocks ? (int)(num_blocks - 1) : b);
+            const int rr = row & 15;                // row within the cache block
+            const int lchunk = pc < 16 ? (pc ^ rr) : (16 + ((pc - 16) ^ (2 * (rr & 7))));
+            const uint16_t* src = cache + (((int64_t)b * Hkv + hk) * AT_BS + rr) * AT_ROW + lchunk * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)src,
+                (__attribute__((address_space(3))) void*)(smem + st * AT_TK * AT_ROW + qd * 512), 16, 0, 0);
         }
     };
 
@@ -98,14 +92,14 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (ntiles > 0) {
-        gload(0);
-        sstore(0);
-    }
-    __syncthreads();
+    if (ntiles > 0) issue(0, 0);
     for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
-        if (tile + 1 < ntiles) gload(tile + 1);
+        const int st = tile & 1;
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's DMA of the tile landed
+        __builtin_amdgcn_s_barrier();         // ... and every wave's; stage st^1 is free
+        at_fence();
+        if (tile + 1 < ntiles) issue(tile + 1, st ^ 1);
+        const uint16_t* tb = smem + st * AT_TK * AT_ROW;
         const int kb = kstart + tile * AT_TK;
 
         // S^T = K Q^T for 4 blocks of 16 keys
@@ -113,19 +107,19 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
         float mt = -INFINITY;
 #pragma unroll
         for (int kblk = 0; kblk < 4; ++kblk) {
-            f32x4 st = {0.f, 0.f, 0.f, 0.f};
-            const int key = kblk * 16 + qi;
+            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+            const int row = kblk * 16 + qi;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int ch = 4 * s + g;
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(&sK[buf][key * AT_D + ((ch ^ (key & 7)) << 3)]));
-                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st, 0, 0, 0);
+                const int ch = (4 * s + g) ^ (row & 15);
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(tb + row * AT_ROW + ch * 8));
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc, 0, 0, 0);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int kp = kb + kblk * 16 + 4 * g + e;
                 const bool vis = qvalid && kp < L && kp >= qlo;
-                sv[kblk][e] = vis ? st[e] * scale_log2 : -INFINITY;
+                sv[kblk][e] = vis ? sacc[e] * scale_log2 : -INFINITY;
                 mt = fmaxf(mt, sv[kblk][e]);
             }
         }
@@ -147,7 +141,9 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
                 lsum += pv[kblk][e];
             }
 
-        // O^T += V^T P^T over two 32-key steps
+        // O^T += V^T P^T over two 32-key steps; K index of the MFMA for lane group g,
+        // element j <-> key 32 s2 + 4 g + j (j < 4) or 32 s2 + 16 + 4 g + (j - 4).
+        const int p = lane & 15;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             u32x4 pp;
@@ -156,19 +152,26 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
             pp[2] = pack_bf16x2(pv[2 * s2 + 1][0], pv[2 * s2 + 1][1]);
             pp[3] = pack_bf16x2(pv[2 * s2 + 1][2], pv[2 * s2 + 1][3]);
             const bf16x8 pf = as_bf16x8(pp);
+            const int r1 = 32 * s2 + 4 * g + (p >> 2);
+            const int r2 = r1 + 16;
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
-                const int d = mb * 16 + qi;
-                const uint16_t* vrow = &sV[buf][d * AT_VP + 32 * s2 + 4 * g];
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-                const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+                // 8-byte chunk of d = 16 mb + 4 (p % 4) in the V half, swizzled by row
+                const int c8 = 4 * mb + (p & 3);
+                const int o1 = r1 * AT_ROW + AT_D + ((c8 ^ (4 * (r1 & 7))) << 2);
+                const int o2 = r2 * AT_ROW + AT_D + ((c8 ^ (4 * (r2 & 7))) << 2);
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(tb + o1));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(tb + o2));
+                u32x4 vv;
+                vv[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+                vv[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+                vv[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+                vv[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
                 o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), pf, o[mb], 0, 0, 0);
             }
         }
-
-        if (tile + 1 < ntiles) sstore(buf ^ 1);
-        __syncthreads();
     }
 
     lsum += __shfl_xor(lsum, 16);
