@@ -19,82 +19,85 @@
 namespace dflash {
 
 constexpr int PJ_ROWS = 64;   // rows of H per workgroup (4 waves x 16)
-constexpr int PJ_BK = 64;     // K chunk staged in LDS
+constexpr int PJ_BK = 64;     // K slice staged in LDS
 constexpr int PJ_THREADS = 256;
+constexpr int PJ_STAGES = 3;
 
-// part[ks][t][i] = sum over the ks-th Hd slice of H[t, j] * Wp[i, j]
+// Issue the LDS-DMA loads of rows [0, nrows) x columns [k0, k0 + 64) of a
+// K-contiguous bf16 matrix (buffer rsrc, row pitch ld elements) into an LDS tile
+// of 128-byte rows (16-byte chunks XOR-swizzled by row % 8).  Instruction q
+// fills rows 8q .. 8q+7; wave w issues q = w, w + 4, ...  Columns >= kend read
+// as zero.
+template <int NQ>
+__device__ __forceinline__ void pj_dma(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, int wave_s, int lane,
+                                       int ld, int k0, int kend) {
+    const int r8 = lane >> 3;
+    const int lc = (lane & 7) ^ r8;
+    const int gk = k0 + lc * 8;
+#pragma unroll
+    for (int q0 = 0; q0 < NQ; q0 += 4) {
+        const int q = q0 + wave_s;
+        if (NQ % 4 == 0 || q < NQ) {
+            const int voff = gk < kend ? ((q * 8 + r8) * ld + gk) * 2 : (int)0x80000000;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(lds_tile + q * 512), 16, voff, 0, 0, 0);
+        }
+    }
+}
+
+// part[ks][t][i] = sum over the ks-th Hd slice of H[t, j] * Wp[i, j].  bf16 MFMA
+// 16x16x32; three-stage LDS-DMA pipeline over 64-wide K slices.
 template <int RB>  // R / 16
 __global__ __launch_bounds__(PJ_THREADS) void edges_projection(const uint16_t* __restrict__ H,
                                                                const uint16_t* __restrict__ Wp, int T,
                                                                int Hd, int kslice,
                                                                float* __restrict__ part) {
     constexpr int R = RB * 16;
-    constexpr int A_CH = PJ_ROWS * 8 / PJ_THREADS;             // 2
-    constexpr int B_CH = (R * 8 + PJ_THREADS - 1) / PJ_THREADS;
-    __shared__ __attribute__((aligned(16))) uint16_t sA[PJ_ROWS * PJ_BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[R * PJ_BK];
+    constexpr int NQA = PJ_ROWS / 8;
+    constexpr int NQB = R / 8;
+    constexpr int STAGE = (PJ_ROWS + R) * PJ_BK;
+    constexpr int PER_WAVE = NQA / 4 + NQB / 4;  // DMA instructions every wave issues per slice
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[PJ_STAGES * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int row0 = blockIdx.x * PJ_ROWS;
     const int ks = blockIdx.y;
     const int kbeg = ks * kslice;
     const int kend = min(Hd, kbeg + kslice);
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const int nS = kend > kbeg ? (kend - kbeg + PJ_BK - 1) / PJ_BK : 0;
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(H + (int64_t)row0 * Hd), (short)0, min(PJ_ROWS, T - row0) * Hd * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsB =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Wp, (short)0, R * Hd * 2, 0x00020000);
 
     f32x4 acc[RB];
 #pragma unroll
     for (int j = 0; j < RB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 ga[A_CH], gb[B_CH];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int ch = tid + PJ_THREADS * i;
-            const int r = ch >> 3, kc = ch & 7;
-            const int gr = row0 + r, gk = k0 + kc * 8;
-            ga[i] = (gr < T && gk < kend) ? ldg16(H + (int64_t)gr * Hd + gk) : zero4;
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int ch = tid + PJ_THREADS * i;
-            const int r = ch >> 3, kc = ch & 7;
-            const int gk = k0 + kc * 8;
-            gb[i] = (r < R && gk < kend) ? ldg16(Wp + (int64_t)r * Hd + gk) : zero4;
-        }
+    auto issue = [&](int sl, int st) {
+        uint16_t* base = smem + st * STAGE;
+        pj_dma<NQA>(rsA, base, wave_s, lane, Hd, kbeg + sl * PJ_BK, kend);
+        pj_dma<NQB>(rsB, base + PJ_ROWS * PJ_BK, wave_s, lane, Hd, kbeg + sl * PJ_BK, kend);
     };
-    auto sstore = [&]() {
+    for (int sl = 0; sl < PJ_STAGES - 1 && sl < nS; ++sl) issue(sl, sl);
+    for (int kt = 0; kt < nS; ++kt) {
+        // wait for slice kt; slice kt+1 may still be in flight
+        if (kt + 1 < nS) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        if (kt + PJ_STAGES - 1 < nS) issue(kt + PJ_STAGES - 1, (kt + PJ_STAGES - 1) % PJ_STAGES);
+        const uint16_t* a_base = smem + (kt % PJ_STAGES) * STAGE;
+        const uint16_t* b_base = a_base + PJ_ROWS * PJ_BK;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int ch = tid + PJ_THREADS * i;
-            const int r = ch >> 3, kc = ch & 7;
-            *reinterpret_cast<u32x4*>(sA + r * PJ_BK + ((kc ^ (r & 7)) << 3)) = ga[i];
-        }
+        for (int kk = 0; kk < 2; ++kk) {
+            const int chs = ((kk * 4 + (lane >> 4)) ^ (lane & 7)) << 3;  // row % 8 == lane % 8
+            const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(a_base + (wave * 16 + (lane & 15)) * PJ_BK + chs));
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int ch = tid + PJ_THREADS * i;
-            const int r = ch >> 3, kc = ch & 7;
-            if (r < R) *reinterpret_cast<u32x4*>(sB + r * PJ_BK + ((kc ^ (r & 7)) << 3)) = gb[i];
-        }
-    };
-
-    if (kbeg < kend) {
-        gload(kbeg);
-        for (int k0 = kbeg; k0 < kend; k0 += PJ_BK) {
-            __syncthreads();  // previous chunk's LDS reads are done
-            sstore();
-            __syncthreads();
-            if (k0 + PJ_BK < kend) gload(k0 + PJ_BK);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int ch = kk * 4 + (lane >> 4);
-                const int ar = wave * 16 + (lane & 15);
-                const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(sA + ar * PJ_BK + ((ch ^ (ar & 7)) << 3)));
-#pragma unroll
-                for (int j = 0; j < RB; ++j) {
-                    const int br = j * 16 + (lane & 15);
-                    const bf16x8 bfr = as_bf16x8(*reinterpret_cast<const u32x4*>(sB + br * PJ_BK + ((ch ^ (br & 7)) << 3)));
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
-                }
+            for (int j = 0; j < RB; ++j) {
+                const bf16x8 bfr = as_bf16x8(*reinterpret_cast<const u32x4*>(b_base + (j * 16 + (lane & 15)) * PJ_BK + chs));
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
             }
         }
     }
@@ -122,12 +125,15 @@ __device__ __forceinline__ void load_bf16_vec(const uint16_t* p, float (&f)[VPL]
 }
 
 // One wave per row t = r * S + p.  KB = ceil(k / 16) blocks of 16 predecessors
-// and 16 candidates; VPL = rank values per lane per 4 * VPL-wide chunk.
-template <int KB, int VPL>
+// and 16 candidates; VPL = rank values per lane per 4 * VPL-wide chunk; RC = the
+// rank when it is a compile-time constant (all loads of the row are then issued
+// before the first MFMA), or 0 for a runtime rank.
+template <int KB, int VPL, int RC>
 __global__ __launch_bounds__(256) void edges_bilinear(
     const uint16_t* __restrict__ P, const uint16_t* __restrict__ Sc, const int32_t* __restrict__ ids,
     const float* __restrict__ U, const float* __restrict__ part, int KS, const int32_t* __restrict__ anchor,
-    int T, int St, int k, int V, int R, float* __restrict__ E) {
+    int T, int St, int k, int V, int R_rt, float* __restrict__ E) {
+    const int R = RC > 0 ? RC : R_rt;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(256) void edges_bilinear(
         for (int b = 0; b < KB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     constexpr int CH = 4 * VPL;
-    for (int i0 = 0; i0 < R; i0 += CH) {
+    auto chunk = [&](int i0) {
         const int ib = i0 + g * VPL;
         float h[VPL];
 #pragma unroll
@@ -193,6 +199,12 @@ __global__ __launch_bounds__(256) void edges_bilinear(
 #pragma unroll
                 for (int bc = 0; bc < KB; ++bc)
                     acc[bq][bc] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bq][v], b[bc][v], acc[bq][bc], 0, 0, 0);
+    };
+    if constexpr (RC > 0) {
+#pragma unroll
+        for (int i0 = 0; i0 < RC; i0 += CH) chunk(i0);
+    } else {
+        for (int i0 = 0; i0 < R; i0 += CH) chunk(i0);
     }
 
 #pragma unroll
@@ -239,17 +251,30 @@ static void launch_projection(const uint16_t* H, const uint16_t* Wp, int T, int 
     hipLaunchKernelGGL((edges_projection<RB>), grid, dim3(PJ_THREADS), 0, st, H, Wp, T, Hd, p.kslice, part);
 }
 
+template <int KB, int RC>
+static void launch_bilinear_r(const uint16_t* P, const uint16_t* Sc, const int32_t* ids, const float* U,
+                              const float* part, int KS, const int32_t* anchor, int T, int St, int k, int V,
+                              int R, float* E, hipStream_t st) {
+    dim3 grid((T + 3) / 4);
+    if (R % 32 == 0)
+        hipLaunchKernelGGL((edges_bilinear<KB, 8, RC>), grid, dim3(256), 0, st, P, Sc, ids, U, part, KS, anchor,
+                           T, St, k, V, R, E);
+    else
+        hipLaunchKernelGGL((edges_bilinear<KB, 4, RC>), grid, dim3(256), 0, st, P, Sc, ids, U, part, KS, anchor,
+                           T, St, k, V, R, E);
+}
+
 template <int KB>
 static void launch_bilinear(const uint16_t* P, const uint16_t* Sc, const int32_t* ids, const float* U,
                             const float* part, int KS, const int32_t* anchor, int T, int St, int k, int V,
                             int R, float* E, hipStream_t st) {
-    dim3 grid((T + 3) / 4);
-    if (R % 32 == 0)
-        hipLaunchKernelGGL((edges_bilinear<KB, 8>), grid, dim3(256), 0, st, P, Sc, ids, U, part, KS, anchor, T,
-                           St, k, V, R, E);
-    else
-        hipLaunchKernelGGL((edges_bilinear<KB, 4>), grid, dim3(256), 0, st, P, Sc, ids, U, part, KS, anchor, T,
-                           St, k, V, R, E);
+    switch (R) {
+        case 16: launch_bilinear_r<KB, 16>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
+        case 64: launch_bilinear_r<KB, 64>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
+        case 128: launch_bilinear_r<KB, 128>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
+        case 256: launch_bilinear_r<KB, 256>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
+        default: launch_bilinear_r<KB, 0>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
+    }
 }
 
 }  // namespace dflash

@@ -81,47 +81,6 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
 // i.e. row 8q + i/8, physical chunk i%8; it therefore loads logical chunk
 // (i%8) ^ (row%8), which realises the XOR swizzle the fragment reads expect.
 // Out-of-range rows and the K tail read as zero (buffer range check).
-// Per-lane byte offsets of the LDS-DMA loads of one 64-wide K slice of the
-// rows this wave loads: instructions q = wave * NI + j, each filling 1 KB = 8
-// rows of 128 B.  Lane i of instruction q lands at LDS byte q*1024 + i*16,
-// i.e. row 8q + i/8, physical chunk i%8; it therefore loads logical chunk
-// (i%8) ^ (row%8), which realises the XOR swizzle the fragment reads expect.
-template <int NI>
-__device__ __forceinline__ void dma_offsets(int (&voff)[NI], int wave_s, int lane, int Hd) {
-    const int r8 = lane >> 3;
-    const int lc = (lane & 7) ^ r8;
-#pragma unroll
-    for (int j = 0; j < NI; ++j) voff[j] = (((wave_s * NI + j) * 8 + r8) * Hd + lc * 8) * 2;
-}
-
-// Issue them for the slice starting at column k0 (scalar offset k0 * 2).  Rows
-// past the tile and, in a final partial slice, columns past Hd read as zero.
-template <int NI>
-__device__ __forceinline__ void dma_slice(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, const int* voff,
-                                          int wave_s, int lane, int Hd, int k0) {
-    if (k0 + 64 <= Hd) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512), 16, voff[j],
-                k0 * 2, 0, 0);
-    } else {
-        const int gk = k0 + (((lane & 7) ^ (lane >> 3)) * 8);
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512), 16,
-                gk < Hd ? voff[j] + k0 * 2 : (int)0x80000000, 0, 0, 0);
-    }
-}
-
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-
 template <int BN, int KCAP>
 __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ W, int T, int V, int Hd,
