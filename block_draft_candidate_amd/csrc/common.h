@@ -72,25 +72,18 @@ __device__ __forceinline__ void dma_offsets(int (&voff)[NI], int wave_s, int lan
     for (int j = 0; j < NI; ++j) voff[j] = (((wave_s * NI + j) * 8 + r8) * Hd + lc * 8) * 2;
 }
 
-// Issue them for the slice starting at column k0 (scalar offset k0 * 2).  Rows
-// past the tile and, in a final partial slice, columns past Hd read as zero.
+// Issue them for the slice starting at column k0.  Rows past the tile and
+// columns past Hd read as zero (offsets past the buffer range); branch-free, so
+// the loads can be interleaved with MFMAs by the scheduler.
 template <int NI>
 __device__ __forceinline__ void dma_slice(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, const int* voff,
                                           int wave_s, int lane, int Hd, int k0) {
-    if (k0 + 64 <= Hd) {
+    const bool in = k0 + (((lane & 7) ^ (lane >> 3)) * 8) < Hd;
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512), 16, voff[j],
-                k0 * 2, 0, 0);
-    } else {
-        const int gk = k0 + (((lane & 7) ^ (lane >> 3)) * 8);
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512), 16,
-                gk < Hd ? voff[j] + k0 * 2 : (int)0x80000000, 0, 0, 0);
-    }
+    for (int j = 0; j < NI; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512), 16,
+            in ? voff[j] + k0 * 2 : (int)0x80000000, 0, 0, 0);
 }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }

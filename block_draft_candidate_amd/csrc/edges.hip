@@ -111,50 +111,84 @@ __global__ __launch_bounds__(PJ_THREADS) void edges_projection(const uint16_t* _
         }
 }
 
-template <int VPL>
-__device__ __forceinline__ void load_bf16_vec(const uint16_t* p, float (&f)[VPL]) {
-    if constexpr (VPL == 8) {
-        unpack8(ldg16(p), f);
-    } else {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-        f[0] = __uint_as_float(v[0] << 16);
-        f[1] = __uint_as_float(v[0] & 0xffff0000u);
-        f[2] = __uint_as_float(v[1] << 16);
-        f[3] = __uint_as_float(v[1] & 0xffff0000u);
-    }
-}
-
-// One wave per row t = r * S + p.  KB = ceil(k / 16) blocks of 16 predecessors
-// and 16 candidates; VPL = rank values per lane per 4 * VPL-wide chunk; RC = the
-// rank when it is a compile-time constant (all loads of the row are then issued
-// before the first MFMA), or 0 for a runtime rank.
-template <int KB, int VPL, int RC>
-__global__ __launch_bounds__(256) void edges_bilinear(
+// One wave per row t = r * S + p (WAVES waves per workgroup, each with its own
+// LDS region).  The row's 16 * KB predecessor and 16 * KB candidate codebook
+// rows are gathered with whole-row coalesced 16-byte loads into LDS (row pitch
+// 2R + 16 bytes, so that the 16 MFMA rows read different banks), h_p (the sum of
+// the KS projection partials, in a fixed order) is staged once per row, then
+// lane l takes predecessor row q = l % 16 (MFMA row) and candidate row c = l % 16
+// (MFMA column) and lane group g = l / 16 owns a quarter of each 4 * VPL-wide rank
+// chunk: a = P[pred] * h_p is formed in fp32 and the k x k block accumulates on
+// v_mfma_f32_16x16x4f32, every product in fp32.
+template <int KB, int R, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void edges_bilinear(
     const uint16_t* __restrict__ P, const uint16_t* __restrict__ Sc, const int32_t* __restrict__ ids,
     const float* __restrict__ U, const float* __restrict__ part, int KS, const int32_t* __restrict__ anchor,
-    int T, int St, int k, int V, int R_rt, float* __restrict__ E) {
-    const int R = RC > 0 ? RC : R_rt;
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int r = t / St, p = t - r * St;
-    const int g = lane >> 4, li = lane & 15;
+    int T, int St, int k, int V, float* __restrict__ E) {
+    constexpr int NR = 16 * KB;              // gathered rows per codebook
+    constexpr int PITCH = R + 8;             // elements (2R + 16 bytes)
+    constexpr int CPR = R / 8;               // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;            // rows per gather instruction
+    constexpr int VPL = (R % 32 == 0) ? 8 : 4;
+    constexpr int CH = 4 * VPL;
+    constexpr int WAVE_ELEMS = 2 * NR * PITCH + 2 * R;  // bf16 rows + fp32 h_p
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem_e[];
 
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * WAVES + wave;
+    const bool live = t < T;
+    const int tt = live ? t : T - 1;        // dead waves mirror the last row and store nothing
+    const int r = tt / St, p = tt - r * St;
+    const int g = lane >> 4, li = lane & 15;
+    uint16_t* sP = smem_e + wave * WAVE_ELEMS;
+    uint16_t* sS = sP + NR * PITCH;
+    float* sH = reinterpret_cast<float*>(sS + NR * PITCH);
+
+    // ids of the predecessor rows (q) and candidate rows (c) this lane stands for
     int pred[KB], cid[KB];
-    bool qv[KB], cv[KB];
 #pragma unroll
     for (int b = 0; b < KB; ++b) {
         const int q = b * 16 + li;
-        qv[b] = q < k;
-        cv[b] = q < k;
         int pr = 0, ci = 0;
         if (q < k) {
-            pr = (p == 0) ? anchor[r] : ids[(int64_t)(t - 1) * k + q];
-            ci = ids[(int64_t)t * k + q];
+            pr = (p == 0) ? anchor[r] : ids[(int64_t)(tt - 1) * k + q];
+            ci = ids[(int64_t)tt * k + q];
         }
         pred[b] = min(max(pr, 0), V - 1);
         cid[b] = min(max(ci, 0), V - 1);
     }
+
+    // h_p, the sum of the KS partials in order, one rank entry per lane per step
+#pragma unroll
+    for (int i = lane; i < R; i += 64) {
+        float h = 0.f;
+        for (int ks = 0; ks < KS; ++ks) h += part[((int64_t)ks * T + tt) * R + i];
+        sH[i] = h;
+    }
+
+    // coalesced gathers: instruction j covers rows j * RPI .. j * RPI + RPI - 1,
+    // CPR lanes per row; row ids come from the lanes that hold them (row % 16)
+    const int gr = lane / CPR, gc = lane % CPR;
+    constexpr int NJ = (NR + RPI - 1) / RPI;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int row = j * RPI + gr;
+        int pid = 0, cidr = 0;
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const int x = __shfl(pred[b], row & 15);
+            const int y = __shfl(cid[b], row & 15);
+            if ((row >> 4) == b) { pid = x; cidr = y; }
+        }
+        if (gr < RPI && row < NR) {
+            const u32x4 pv = ldg16(P + (int64_t)pid * R + gc * 8);
+            const u32x4 sv = ldg16(Sc + (int64_t)cidr * R + gc * 8);
+            *reinterpret_cast<u32x4*>(sP + row * PITCH + gc * 8) = pv;
+            *reinterpret_cast<u32x4*>(sS + row * PITCH + gc * 8) = sv;
+        }
+    }
+    __syncthreads();
 
     f32x4 acc[KB][KB];
 #pragma unroll
@@ -162,35 +196,35 @@ __global__ __launch_bounds__(256) void edges_bilinear(
 #pragma unroll
         for (int b = 0; b < KB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int CH = 4 * VPL;
-    auto chunk = [&](int i0) {
+#pragma unroll
+    for (int i0 = 0; i0 < R; i0 += CH) {
         const int ib = i0 + g * VPL;
         float h[VPL];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) h[v] = 0.f;
-        for (int ks = 0; ks < KS; ++ks) {
-            const float* src = part + ((int64_t)ks * T + t) * R + ib;
-#pragma unroll
-            for (int v = 0; v < VPL; v += 4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(src + v);
-                h[v] += x[0];
-                h[v + 1] += x[1];
-                h[v + 2] += x[2];
-                h[v + 3] += x[3];
-            }
+        for (int v = 0; v < VPL; v += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sH + ib + v);
+            h[v] = x[0]; h[v + 1] = x[1]; h[v + 2] = x[2]; h[v + 3] = x[3];
         }
         float a[KB][VPL], b[KB][VPL];
 #pragma unroll
         for (int bq = 0; bq < KB; ++bq) {
-            load_bf16_vec<VPL>(P + (int64_t)pred[bq] * R + ib, a[bq]);
+            const bool qv = bq * 16 + li < k;
+            if constexpr (VPL == 8) {
+                unpack8(*reinterpret_cast<const u32x4*>(sP + (bq * 16 + li) * PITCH + ib), a[bq]);
+                unpack8(*reinterpret_cast<const u32x4*>(sS + (bq * 16 + li) * PITCH + ib), b[bq]);
+            } else {
+                const u32x2 x = *reinterpret_cast<const u32x2*>(sP + (bq * 16 + li) * PITCH + ib);
+                const u32x2 y = *reinterpret_cast<const u32x2*>(sS + (bq * 16 + li) * PITCH + ib);
+                a[bq][0] = __uint_as_float(x[0] << 16); a[bq][1] = __uint_as_float(x[0] & 0xffff0000u);
+                a[bq][2] = __uint_as_float(x[1] << 16); a[bq][3] = __uint_as_float(x[1] & 0xffff0000u);
+                b[bq][0] = __uint_as_float(y[0] << 16); b[bq][1] = __uint_as_float(y[0] & 0xffff0000u);
+                b[bq][2] = __uint_as_float(y[1] << 16); b[bq][3] = __uint_as_float(y[1] & 0xffff0000u);
+            }
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) a[bq][v] = qv[bq] ? a[bq][v] * h[v] : 0.f;
-        }
-#pragma unroll
-        for (int bc = 0; bc < KB; ++bc) {
-            load_bf16_vec<VPL>(Sc + (int64_t)cid[bc] * R + ib, b[bc]);
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) b[bc][v] = cv[bc] ? b[bc][v] : 0.f;
+            for (int v = 0; v < VPL; ++v) {
+                a[bq][v] = qv ? a[bq][v] * h[v] : 0.f;
+                b[bq][v] = qv ? b[bq][v] : 0.f;
+            }
         }
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
@@ -199,14 +233,9 @@ __global__ __launch_bounds__(256) void edges_bilinear(
 #pragma unroll
                 for (int bc = 0; bc < KB; ++bc)
                     acc[bq][bc] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bq][v], b[bc][v], acc[bq][bc], 0, 0, 0);
-    };
-    if constexpr (RC > 0) {
-#pragma unroll
-        for (int i0 = 0; i0 < RC; i0 += CH) chunk(i0);
-    } else {
-        for (int i0 = 0; i0 < R; i0 += CH) chunk(i0);
     }
 
+    if (!live) return;
 #pragma unroll
     for (int bc = 0; bc < KB; ++bc) {
         const int c = bc * 16 + li;
@@ -251,29 +280,30 @@ static void launch_projection(const uint16_t* H, const uint16_t* Wp, int T, int 
     hipLaunchKernelGGL((edges_projection<RB>), grid, dim3(PJ_THREADS), 0, st, H, Wp, T, Hd, p.kslice, part);
 }
 
-template <int KB, int RC>
+template <int KB, int R>
 static void launch_bilinear_r(const uint16_t* P, const uint16_t* Sc, const int32_t* ids, const float* U,
                               const float* part, int KS, const int32_t* anchor, int T, int St, int k, int V,
-                              int R, float* E, hipStream_t st) {
-    dim3 grid((T + 3) / 4);
-    if (R % 32 == 0)
-        hipLaunchKernelGGL((edges_bilinear<KB, 8, RC>), grid, dim3(256), 0, st, P, Sc, ids, U, part, KS, anchor,
-                           T, St, k, V, R, E);
-    else
-        hipLaunchKernelGGL((edges_bilinear<KB, 4, RC>), grid, dim3(256), 0, st, P, Sc, ids, U, part, KS, anchor,
-                           T, St, k, V, R, E);
+                              float* E, hipStream_t st) {
+    constexpr size_t wave_bytes = (size_t)(2 * 16 * KB * (R + 8) + 2 * R) * 2;
+    constexpr int WAVES = wave_bytes * 4 <= 64 * 1024 ? 4 : 1;
+    if (wave_bytes * WAVES > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&edges_bilinear<KB, R, WAVES>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)(wave_bytes * WAVES));
+    hipLaunchKernelGGL((edges_bilinear<KB, R, WAVES>), dim3((T + WAVES - 1) / WAVES), dim3(64 * WAVES),
+                       wave_bytes * WAVES, st, P, Sc, ids, U, part, KS, anchor, T, St, k, V, E);
 }
 
 template <int KB>
-static void launch_bilinear(const uint16_t* P, const uint16_t* Sc, const int32_t* ids, const float* U,
+static bool launch_bilinear(const uint16_t* P, const uint16_t* Sc, const int32_t* ids, const float* U,
                             const float* part, int KS, const int32_t* anchor, int T, int St, int k, int V,
                             int R, float* E, hipStream_t st) {
     switch (R) {
-        case 16: launch_bilinear_r<KB, 16>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
-        case 64: launch_bilinear_r<KB, 64>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
-        case 128: launch_bilinear_r<KB, 128>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
-        case 256: launch_bilinear_r<KB, 256>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
-        default: launch_bilinear_r<KB, 0>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, R, E, st); break;
+#define BL_CASE(n) \
+    case n: launch_bilinear_r<KB, n>(P, Sc, ids, U, part, KS, anchor, T, St, k, V, E, st); return true;
+        BL_CASE(16) BL_CASE(32) BL_CASE(48) BL_CASE(64) BL_CASE(80) BL_CASE(96) BL_CASE(112) BL_CASE(128)
+        BL_CASE(144) BL_CASE(160) BL_CASE(176) BL_CASE(192) BL_CASE(208) BL_CASE(224) BL_CASE(240) BL_CASE(256)
+#undef BL_CASE
+        default: return false;
     }
 }
 
@@ -313,12 +343,14 @@ extern "C" int dflash_candidate_edges(const uint16_t* pred_cb, const uint16_t* s
     }
     DFLASH_LAUNCH_CHECK();
     const int KB = (k + 15) / 16;
+    bool ok;
     if (KB == 1)
-        launch_bilinear<1>(pred_cb, succ_cb, cand_ids, unary, part, p.KS, anchor, Ti, S, k, (int)V, R, edges, st);
+        ok = launch_bilinear<1>(pred_cb, succ_cb, cand_ids, unary, part, p.KS, anchor, Ti, S, k, (int)V, R, edges, st);
     else if (KB == 2)
-        launch_bilinear<2>(pred_cb, succ_cb, cand_ids, unary, part, p.KS, anchor, Ti, S, k, (int)V, R, edges, st);
+        ok = launch_bilinear<2>(pred_cb, succ_cb, cand_ids, unary, part, p.KS, anchor, Ti, S, k, (int)V, R, edges, st);
     else
-        launch_bilinear<4>(pred_cb, succ_cb, cand_ids, unary, part, p.KS, anchor, Ti, S, k, (int)V, R, edges, st);
+        ok = launch_bilinear<4>(pred_cb, succ_cb, cand_ids, unary, part, p.KS, anchor, Ti, S, k, (int)V, R, edges, st);
+    if (!ok) return DFLASH_ERR_UNSUPPORTED;
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
 }

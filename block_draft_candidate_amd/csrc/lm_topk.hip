@@ -81,10 +81,22 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
 // i.e. row 8q + i/8, physical chunk i%8; it therefore loads logical chunk
 // (i%8) ^ (row%8), which realises the XOR swizzle the fragment reads expect.
 // Out-of-range rows and the K tail read as zero (buffer range check).
+// Scheduling pattern for one K step: NG groups of MPG MFMAs, each followed by one
+// LDS fragment read and (in the first NV groups) one LDS-DMA load.
+template <int NG, int MPG, int NV>
+__device__ __forceinline__ void sched_interleave() {
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+}
+
 template <int BN, int KCAP>
 __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ W, int T, int V, int Hd,
-    int nM, int nN, int G, int xcd_map, float s, float c, float inv_c,
+    int nM, int nN, int G, int xmx, float s, float c, float inv_c,
     uint64_t* __restrict__ part) {
     constexpr int WN = BN / 2;               // columns per wave
     constexpr int NB = WN / 32;              // 32-column MFMA blocks per wave
@@ -106,13 +118,21 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int wm = wave >> 1, wn = wave & 1;
 
-    int L = blockIdx.x;
-    if (xcd_map) {
+    // Workgroup ids go to the 8 XCDs round-robin.  With xmx > 0 the (group,
+    // row-tile) grid is cut into 8 blocks of (per / xmx) groups x xmx row tiles,
+    // one per XCD, so each XCD's L2 serves W tiles to xmx row tiles and H slices
+    // to per / xmx groups.
+    int m_tile, g;
+    if (xmx > 0) {
         const int per = gridDim.x >> 3;
-        L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        const int gx = per / xmx, bms = nM / xmx;
+        g = (x / bms) * gx + j / xmx;
+        m_tile = (x % bms) * xmx + j % xmx;
+    } else {
+        m_tile = blockIdx.x % nM;
+        g = blockIdx.x / nM;
     }
-    const int m_tile = L % nM;
-    const int g = L / nM;
     const int n_begin = (int)((int64_t)g * nN / G);
     const int n_end = (int)((int64_t)(g + 1) * nN / G);
     const int m0 = m_tile * LM_BM;
@@ -149,10 +169,11 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-        auto issue = [&](int kt, int st) {
-            uint16_t* base = smem + st * STAGE;
-            dma_slice<NIA>(rsA, base, voffA, wave_s, lane, Hd, kt * LM_BK);
-            dma_slice<NIB>(rsB, base + LM_BM * LM_BK, voffB, wave_s, lane, Hd, kt * LM_BK);
+        auto issue_a = [&](int kt, int st) {
+            dma_slice<NIA>(rsA, smem + st * STAGE, voffA, wave_s, lane, Hd, kt * LM_BK);
+        };
+        auto issue_b = [&](int kt, int st) {
+            dma_slice<NIB>(rsB, smem + st * STAGE + LM_BM * LM_BK, voffB, wave_s, lane, Hd, kt * LM_BK);
         };
         // fragments of one 16-wide K step (k16 = 0..3) of the slice in stage st
         auto read_frags = [&](int st, int k16, bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
@@ -172,24 +193,24 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                 for (int j = 0; j < NB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         };
-        // one fragment read of the next K step after every MFMA pair
-        auto interleave = [&]() {
-#pragma unroll
-            for (int q = 0; q < MB + NB; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, (MB * NB) / (MB + NB), 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        };
+        // spread the next K step's fragment reads (and NV LDS-DMA loads) between
+        // the MFMAs of the current one
+        constexpr int NG = MB + NB;                  // groups of MFMAs per K step
+        constexpr int MPG = (MB * NB) / NG;          // MFMAs per group
 
-        // Software pipeline: fragments of the next 16-wide K step are read while
-        // the MFMAs of the current one run.  Two LDS stages, one barrier per
-        // 64-wide slice: before the first K step of slice kt+1 every wave waits
-        // for its DMA of that slice, then a barrier (all waves are done reading
-        // stage kt%2) lets the DMA of slice kt+2 start into it.
+        // Software pipeline over 64-wide K slices with two LDS stages and one
+        // barrier per slice.  The fragments of the next 16-wide K step are read
+        // while the MFMAs of the current one run.  The DMA of slice kt+2 goes
+        // into stage kt%2 as soon as the barrier in the last K step of slice kt
+        // shows every wave is done reading it: its A half right after that
+        // barrier, its B half during the first K step of slice kt+1, both spread
+        // between MFMAs.  The wait before that barrier covers slice kt+1.
         bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
-        issue(0, 0);
+        issue_a(0, 0);
+        issue_b(0, 0);
         if (nK > 1) {
-            issue(1, 1);
+            issue_a(1, 1);
+            issue_b(1, 1);
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(NIA + NIB));  // slice 0 landed, slice 1 may be in flight
         } else {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -197,24 +218,39 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
         __builtin_amdgcn_s_barrier();
         compiler_fence();
         read_frags(0, 0, fa0, fb0);
-        for (int kt = 0; kt < nK; ++kt) {
+        for (int kt = 0; kt + 1 < nK; ++kt) {
             const int st = kt & 1;
             read_frags(st, 1, fa1, fb1);
+            // B half of slice kt+1 (slice 1 was loaded whole: a harmless repeat)
+            issue_b(kt + 1, st ^ 1);
             mfmas(fa0, fb0);
-            interleave();
+            sched_interleave<NG, MPG, NIB>();
             read_frags(st, 2, fa0, fb0);
             mfmas(fa1, fb1);
-            interleave();
+            sched_interleave<NG, MPG, 0>();
             read_frags(st, 3, fa1, fb1);
             mfmas(fa0, fb0);
-            interleave();
-            if (kt + 1 < nK) {
-                __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-                __builtin_amdgcn_s_barrier();
-                compiler_fence();
-                if (kt + 2 < nK) issue(kt + 2, st);
-                read_frags(st ^ 1, 0, fa0, fb0);
-            }
+            sched_interleave<NG, MPG, 0>();
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): slice kt+1 landed
+            __builtin_amdgcn_s_barrier();
+            compiler_fence();
+            // A half of slice kt+2 (past the end: range-checked zeros into a dead stage)
+            issue_a(kt + 2, st);
+            read_frags(st ^ 1, 0, fa0, fb0);
+            mfmas(fa1, fb1);
+            sched_interleave<NG, MPG, NIA>();
+        }
+        {
+            const int st = (nK - 1) & 1;
+            read_frags(st, 1, fa1, fb1);
+            mfmas(fa0, fb0);
+            sched_interleave<NG, MPG, 0>();
+            read_frags(st, 2, fa0, fb0);
+            mfmas(fa1, fb1);
+            sched_interleave<NG, MPG, 0>();
+            read_frags(st, 3, fa1, fb1);
+            mfmas(fa0, fb0);
+            sched_interleave<NG, MPG, 0>();
             mfmas(fa1, fb1);
         }
         __builtin_amdgcn_s_waitcnt(0x0070);
@@ -345,7 +381,7 @@ __global__ __launch_bounds__(256) void lm_topk_merge(const uint64_t* __restrict_
 }
 
 struct LmPlan {
-    int BN, KCAP, nM, nN, G, xcd;
+    int BN, KCAP, nM, nN, G, xmx;
     int64_t nwg;
     size_t ws;
 };
@@ -370,7 +406,20 @@ static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p) {
     if ((int64_t)p.nM * p.G < target) groups(128);
     p.nwg = (int64_t)p.nM * p.G;
     if (p.nwg > (int64_t)1 << 30) return false;
-    p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+    // XCD blocks: xmx row tiles x (per / xmx) groups per XCD, xmx the divisor of
+    // gcd(nM, per) closest to sqrt(2 * per)
+    p.xmx = 0;
+    if (p.nwg % 8 == 0) {
+        const int per = (int)(p.nwg / 8);
+        int best = 0;
+        double bestd = 1e30;
+        for (int d = 1; d <= per && d <= p.nM; ++d) {
+            if (per % d || p.nM % d || p.G % (per / d)) continue;
+            const double dist = fabs(log((double)d / sqrt(2.0 * per)));
+            if (dist < bestd) { bestd = dist; best = d; }
+        }
+        if (best > 0 && (p.G / (per / best)) * (p.nM / best) == 8) p.xmx = best;
+    }
     p.ws = (size_t)T * (size_t)p.G * (size_t)p.KCAP * sizeof(uint64_t);
     return true;
 }
@@ -380,7 +429,7 @@ static void launch_tiles(const LmPlan& p, const uint16_t* H, const uint16_t* W, 
                          float s, float c, uint64_t* part, hipStream_t st) {
     const float inv_c = c > 0.f ? 1.0f / c : 0.f;
     hipLaunchKernelGGL((lm_topk_tiles<BN, KCAP>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H, W, T,
-                       V, Hd, p.nM, p.nN, p.G, p.xcd, s, c, inv_c, part);
+                       V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part);
 }
 
 template <int KCAP>
