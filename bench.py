@@ -14,6 +14,7 @@ Per-kernel times come from HIP events on the stream the kernels run on; the
 roofline object is for the dominant kernel (the LM-head top-k, MFMA-bound).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+    python bench.py --copy-probe-mib 1024     # plain copy, for counter calibration
 """
 from __future__ import annotations
 
@@ -122,6 +123,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times and exit "
+                         "(the reference point that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path would shard across GPUs "
@@ -134,9 +138,17 @@ def main():
     import block_draft_candidate_amd as B
     import workloads as WL
 
-    B.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_probe_mib} MiB three times")
+        return
+    B.lib()
 
     def dbf(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)

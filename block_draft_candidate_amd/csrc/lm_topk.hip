@@ -25,6 +25,11 @@
 namespace dflash {
 
 constexpr int LM_BM = 256;
+
+// Byte offset in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 constexpr int LM_BK = 64;
 constexpr int LM_THREADS = 256;
 
@@ -37,22 +42,47 @@ __device__ __forceinline__ uint32_t unorder_key(uint32_t o) {
     return (o & 0x8000u) ? (o & 0x7fffu) : (~o & 0xffffu);
 }
 
+// tanh in fp32 for the soft cap, within a few ulp: the odd Taylor series of
+// tanh through y^15 below |y| = 0.55 (truncation under half an ulp there), and
+// 1 - 2 / (e^{2|y|} + 1) above, where tanh >= 0.5 keeps the subtraction exact
+// enough (hardware exp2 and reciprocal, about 1 ulp each).
+__device__ __forceinline__ float cap_tanh(float y) {
+    const float a = fabsf(y);
+    float t;
+    if (a < 0.55f) {
+        const float z = a * a;
+        float q = -929569.f / 638512875.f;
+        q = fmaf(q, z, 21844.f / 6081075.f);
+        q = fmaf(q, z, -1382.f / 155925.f);
+        q = fmaf(q, z, 62.f / 2835.f);
+        q = fmaf(q, z, -17.f / 315.f);
+        q = fmaf(q, z, 2.f / 15.f);
+        q = fmaf(q, z, -1.f / 3.f);
+        t = fmaf(a * z, q, a);
+    } else {
+        const float e = __builtin_amdgcn_exp2f(a * 2.8853900817779268f);  // e^{2a}; inf for large a
+        t = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+    }
+    return copysignf(t, y);
+}
+
 // The top-k key of one accumulator: bf16(c * tanh(s * acc / c)), or bf16(s * acc)
 // without a cap.
 __device__ __forceinline__ uint32_t logit_key_bits(float acc, float s, float c, float inv_c) {
     float x = s * acc;
-    if (c > 0.f) x = c * tanhf(x * inv_c);
+    if (c > 0.f) x = c * cap_tanh(x * inv_c);
     return f32_to_bf16_bits(x);
 }
 
 // A raw-accumulator bound below which a logit's key is certainly smaller than
-// the key `okey`: the value two bf16 steps below the key, mapped back through
-// the cap and the scale, with a relative margin of 2^-12 at each step (far
-// above the fp32 error of tanh/atanh).  Near saturation of the cap (|x| >
-// 0.9 c) no bound is used.
+// the key `okey`: a logit that rounds to the key or above lies above the bf16
+// value one step below it, which is mapped back through the cap and the scale
+// with a relative margin of 2^-12 at each step (far above the fp32 error of
+// the tanh and atanh used).  Near saturation of the cap (|x| > 0.9 c) no bound
+// is used.
 __device__ float acc_lower_bound(uint32_t okey, float s, float c) {
-    if (okey < 0x0082u) return -INFINITY;  // at or below -inf: nothing to bound
-    const float xlo = bf16_bits_to_f32(unorder_key(okey - 2));
+    if (okey < 0x0081u) return -INFINITY;  // the step below is -inf: nothing to bound
+    const float xlo = bf16_bits_to_f32(unorder_key(okey - 1));
     if (!(xlo > -INFINITY)) return -INFINITY;
     float y = xlo;
     if (c > 0.f) {
@@ -104,12 +134,11 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     constexpr int NIA = LM_BM / 8 / 4;       // LDS-DMA instructions per wave per slice (A)
     constexpr int NIB = BN / 8 / 4;          // (B)
     constexpr int STAGE = (LM_BM + BN) * LM_BK;  // elements per pipeline stage
-    constexpr int QCOLS = 64;                // epilogue pass width (columns)
-    constexpr int PASSES = BN / QCOLS;
-    constexpr int PASS_PER_WAVE = PASSES / 2;
-    constexpr int JPP = NB / PASS_PER_WAVE;  // MFMA column blocks per pass (2)
-    static_assert(LM_BM * QCOLS * 4 <= STAGE * 2 * 2, "epilogue staging must fit the stages");
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+    constexpr int QCOLS = WN;                // epilogue pass width: one wave's columns
+    constexpr int MW = QCOLS / 32;           // 32-bit words of a pass's candidate mask
+    constexpr int SP = QCOLS + 4;            // row pitch (floats) of the epilogue staging
+    constexpr int SMEM = (2 * STAGE > LM_BM * SP * 2) ? 2 * STAGE : LM_BM * SP * 2;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
     float* stage = reinterpret_cast<float*>(smem);
 
     const int tid = threadIdx.x;
@@ -257,62 +286,112 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
         __builtin_amdgcn_s_barrier();
         compiler_fence();
 
-        // Epilogue: stage 64 columns at a time, column-major (64 cols x 256 rows
-        // fp32; 4-row groups XOR-swizzled by column so that both the 16-byte
-        // writes of the MFMA layout and the row scans are bank-spread), then
-        // thread t scans row t.  In the 32x32 MFMA layout lane l holds column
-        // l % 32 and rows 8b + 4(l / 32) + e, e = 0..3 (four consecutive rows).
+        // Epilogue, two passes: the columns of wave wn = pass are staged
+        // row-major with a row pitch of QCOLS + 4 floats (the 32-lane halves of
+        // a 4-byte write cover 32 consecutive columns of one row; 16-byte reads
+        // of 8 consecutive rows hit distinct banks), then thread t scans row t.
+        // In the 32x32 MFMA layout lane l holds column l % 32 and rows
+        // 8b + 4(l / 32) + e, e = 0..3.
 #pragma unroll
-        for (int pass = 0; pass < PASSES; ++pass) {
-            if (wn == pass / PASS_PER_WAVE) {
-                const int jb = (pass % PASS_PER_WAVE) * JPP;
+        for (int pass = 0; pass < 2; ++pass) {
+            if (wn == pass) {
 #pragma unroll
-                for (int jj = 0; jj < JPP; ++jj) {
-                    const int col = jj * 32 + fr;
+                for (int j = 0; j < NB; ++j) {
+                    const int col = j * 32 + fr;
 #pragma unroll
                     for (int i = 0; i < MB; ++i)
 #pragma unroll
                         for (int b = 0; b < 4; ++b) {
-                            const int rg = (wm * 128 + i * 32 + 8 * b + 4 * (lane >> 5)) >> 2;  // 4-row group
-                            const f32x4 v = {acc[i][jb + jj][4 * b], acc[i][jb + jj][4 * b + 1],
-                                             acc[i][jb + jj][4 * b + 2], acc[i][jb + jj][4 * b + 3]};
-                            *reinterpret_cast<f32x4*>(stage + col * LM_BM + ((rg ^ (col & 31)) << 2)) = v;
+                            // 4-byte writes straight from the accumulator AGPRs: element
+                            // access from C++ makes the allocator move the accumulators
+                            // to VGPRs and spill.  (lgkmcnt is waited for explicitly
+                            // before the barrier below.)
+                            const uint32_t dst = lds_offset(
+                                stage + (wm * 128 + i * 32 + 8 * b + 4 * (lane >> 5)) * SP + col);
+                            asm volatile("ds_write_b32 %0, %1" ::"v"(dst), "a"(acc[i][j][4 * b]) : "memory");
+                            asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(dst), "a"(acc[i][j][4 * b + 1]),
+                                         "i"(SP * 4) : "memory");
+                            asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(dst), "a"(acc[i][j][4 * b + 2]),
+                                         "i"(SP * 8) : "memory");
+                            asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(dst), "a"(acc[i][j][4 * b + 3]),
+                                         "i"(SP * 12) : "memory");
                         }
                 }
             }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging writes done
             __builtin_amdgcn_s_barrier();
             compiler_fence();
             if (my_row < T) {
                 const int cbase = n0 + pass * QCOLS;
                 const int ncols = min(QCOLS, V - cbase);
-                // element (row t, column cc) of the column-major staging
-                const int rg = tid >> 2, r4 = tid & 3;
-                auto at = [&](int cc) { return stage[cc * LM_BM + ((rg ^ (cc & 31)) << 2) + r4]; };
-                // 1) mask of this row's columns whose raw accumulator reaches the
-                //    threshold (cheap, no divergence)
-                uint32_t m_lo = 0u, m_hi = 0u;
+                const float* rowp = stage + tid * SP;
+                auto at = [&](int cc) { return rowp[cc]; };
+                // 0) a row's first pass (empty list): start from the key of the
+                //    smallest of KCAP group maxima of the pass's columns.  At
+                //    least KCAP values reach it, so a key below it is out.
+                constexpr int GS = QCOLS / KCAP;  // columns per group
+                if (GS >= 4 && thr == -INFINITY && ncols == QCOLS) {
+                    float mn = INFINITY;
 #pragma unroll
-                for (int cc = 0; cc < QCOLS; ++cc) {
-                    const uint32_t bit = (at(cc) >= thr && cc < ncols) ? 1u : 0u;
-                    if (cc < 32) m_lo |= bit << cc; else m_hi |= bit << (cc - 32);
+                    for (int gq = 0; gq < KCAP; ++gq) {
+                        float mx = -INFINITY;
+#pragma unroll
+                        for (int q = 0; q < GS / 4; ++q) {
+                            const f32x4 x = *reinterpret_cast<const f32x4*>(rowp + gq * GS + 4 * q);
+                            mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+                        }
+                        mn = fminf(mn, mx);
+                    }
+                    if (mn > -INFINITY && mn < INFINITY)
+                        thr = acc_lower_bound(order_key(logit_key_bits(mn, s, c, inv_c)), s, c);
+                }
+                // 1) mask of this row's columns whose raw accumulator reaches the
+                //    threshold (16-byte reads, no divergence)
+                uint32_t m[MW];
+#pragma unroll
+                for (int w = 0; w < MW; ++w) {
+                    f32x4 v4[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) v4[q] = *reinterpret_cast<const f32x4*>(rowp + 32 * w + 4 * q);
+                    uint32_t mw = 0u;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int cc = 32 * w + 4 * q + e;
+                            mw |= ((v4[q][e] >= thr && cc < ncols) ? 1u : 0u) << (4 * q + e);
+                        }
+                    m[w] = mw;
                 }
                 // 2) candidates in column (= token id) order, one per lane per
-                //    round; the threshold rises as the list fills, so later
-                //    candidates are mostly dropped by a single compare.
-                while ((m_lo | m_hi) != 0u) {
-                    int cc;
-                    if (m_lo) { cc = __builtin_ctz(m_lo); m_lo &= m_lo - 1u; }
-                    else { cc = 32 + __builtin_ctz(m_hi); m_hi &= m_hi - 1u; }
-                    const float v = at(cc);
+                //    round, the LDS read of the next one issued ahead; the
+                //    threshold is raised once per pass, after the rounds.
+                auto pop = [&]() {
+                    int cc = -1;
+#pragma unroll
+                    for (int w = MW - 1; w >= 0; --w)
+                        if (m[w]) cc = 32 * w + __builtin_ctz(m[w]);
+                    if (cc >= 0) m[cc >> 5] &= m[cc >> 5] - 1u;
+                    return cc;
+                };
+                bool changed = false;
+                int cc = pop();
+                float v = at(cc < 0 ? 0 : cc);
+                while (cc >= 0) {
+                    const int cn = pop();
+                    const float vn = at(cn < 0 ? 0 : cn);
                     if (v >= thr) {
                         const uint32_t kb = logit_key_bits(v, s, c, inv_c);
                         const uint32_t p = (order_key(kb) << 16) | (0xffffu - (uint32_t)(cbase + cc - gcol0));
                         if (p > list[KCAP - 1]) {
                             list_insert(list, p);
-                            if (list[KCAP - 1] != 0u) thr = acc_lower_bound(list[KCAP - 1] >> 16, s, c);
+                            changed = true;
                         }
                     }
+                    cc = cn;
+                    v = vn;
                 }
+                if (changed && list[KCAP - 1] != 0u) thr = acc_lower_bound(list[KCAP - 1] >> 16, s, c);
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): row reads done before the next pass writes
             __builtin_amdgcn_s_barrier();
