@@ -56,34 +56,60 @@ __device__ __forceinline__ void stg16(void* p, u32x4 v) {
 // ---------------------------------------------------------------------------
 // LDS-DMA tile loads (buffer_load_dwordx4 ... lds): 64-wide K slices of
 // K-contiguous bf16 rows, 128 bytes per row in LDS, 16-byte chunks XOR-swizzled
-// by row (chunk ^ row % 8) so that 16x16x32 / 32x32x16 fragment reads are
-// bank-conflict free.
+// by row: physical chunk = logical chunk ^ swz8(row).
+//
+// swz8 folds bits 2..4 of the row into bits 0..2: with chunk ^ (row % 8) alone,
+// rows r and r + 8 of the 32 rows a 32x32x16 fragment read touches land on the
+// same banks, and ds_read_b128 runs at about 55% of the rate it reaches for
+// linear addresses (measured on gfx950); with swz8 it reaches that rate.  For a
+// row inside an aligned 32-row block swz8 depends only on row % 32.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 2)) & 7; }
+
 // Per-lane byte offsets of the LDS-DMA loads of one 64-wide K slice of the
 // rows this wave loads: instructions q = wave * NI + j, each filling 1 KB = 8
 // rows of 128 B.  Lane i of instruction q lands at LDS byte q*1024 + i*16,
 // i.e. row 8q + i/8, physical chunk i%8; it therefore loads logical chunk
-// (i%8) ^ (row%8), which realises the XOR swizzle the fragment reads expect.
+// (i%8) ^ swz8(row).  The logical chunks (3 bits per j) go to lcpack for the
+// K-tail check.
 template <int NI>
-__device__ __forceinline__ void dma_offsets(int (&voff)[NI], int wave_s, int lane, int Hd) {
+__device__ __forceinline__ void dma_offsets(int (&voff)[NI], int& lcpack, int wave_s, int lane, int Hd) {
+    static_assert(NI <= 10, "3 bits per instruction in lcpack");
     const int r8 = lane >> 3;
-    const int lc = (lane & 7) ^ r8;
+    lcpack = 0;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) voff[j] = (((wave_s * NI + j) * 8 + r8) * Hd + lc * 8) * 2;
+    for (int j = 0; j < NI; ++j) {
+        const int row = (wave_s * NI + j) * 8 + r8;
+        const int lc = (lane & 7) ^ swz8(row);
+        voff[j] = (row * Hd + lc * 8) * 2;
+        lcpack |= lc << (3 * j);
+    }
 }
 
-// Issue them for the slice starting at column k0.  Rows past the tile and
-// columns past Hd read as zero (offsets past the buffer range); branch-free, so
-// the loads can be interleaved with MFMAs by the scheduler.
-template <int NI>
+// One of those loads (instruction j of this wave) for the slice starting at
+// column k0; see dma_slice.
+template <int NI, bool TAIL>
+__device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, const int* voff,
+                                        int lcpack, int wave_s, int Hd, int k0, int j) {
+    auto* dst = (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512);
+    if (TAIL) {
+        const bool in = k0 + ((lcpack >> (3 * j)) & 7) * 8 < Hd;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, in ? voff[j] + k0 * 2 : (int)0x80000000, 0, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff[j], k0 * 2, 0, 0);
+    }
+}
+
+// Issue them for the slice starting at column k0.  Rows past the tile read as
+// zero (offsets past the buffer range).  Without a K tail (Hd % 64 == 0) the
+// column offset goes into the scalar offset and no vector work is needed; with
+// one, chunks past Hd get an out-of-range offset.  Branch-free, so the loads
+// can be interleaved with MFMAs by the scheduler.
+template <int NI, bool TAIL>
 __device__ __forceinline__ void dma_slice(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, const int* voff,
-                                          int wave_s, int lane, int Hd, int k0) {
-    const bool in = k0 + (((lane & 7) ^ (lane >> 3)) * 8) < Hd;
+                                          int lcpack, int wave_s, int Hd, int k0) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512), 16,
-            in ? voff[j] + k0 * 2 : (int)0x80000000, 0, 0, 0);
+    for (int j = 0; j < NI; ++j) dma_one<NI, TAIL>(rsrc, lds_tile, voff, lcpack, wave_s, Hd, k0, j);
 }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }

@@ -105,25 +105,10 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
     L[0] = max(L[0], p);
 }
 
-// Issue the LDS-DMA loads of one 64-wide K slice of `nrows` rows (this wave's
-// share: instructions q = wave * NI .. wave * NI + NI - 1, each filling 1 KB =
-// 8 rows of 128 B).  Lane i of instruction q lands at LDS byte q*1024 + i*16,
-// i.e. row 8q + i/8, physical chunk i%8; it therefore loads logical chunk
-// (i%8) ^ (row%8), which realises the XOR swizzle the fragment reads expect.
-// Out-of-range rows and the K tail read as zero (buffer range check).
-// Scheduling pattern for one K step: NG groups of MPG MFMAs, each followed by one
-// LDS fragment read and (in the first NV groups) one LDS-DMA load.
-template <int NG, int MPG, int NV>
-__device__ __forceinline__ void sched_interleave() {
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-}
+// s_waitcnt immediate that waits for vmcnt <= n and lgkmcnt == 0.
+constexpr int vm_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
-template <int BN, int KCAP>
+template <int BN, int KCAP, bool TAIL>
 __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ W, int T, int V, int Hd,
     int nM, int nN, int G, int xmx, float s, float c, float inv_c,
@@ -133,11 +118,12 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     constexpr int MB = 4;                    // 32-row MFMA blocks per wave (128 rows)
     constexpr int NIA = LM_BM / 8 / 4;       // LDS-DMA instructions per wave per slice (A)
     constexpr int NIB = BN / 8 / 4;          // (B)
-    constexpr int STAGE = (LM_BM + BN) * LM_BK;  // elements per pipeline stage
+    constexpr int UNIT = (LM_BM > BN ? LM_BM : BN) * LM_BK;  // elements of one operand's K slice
+    constexpr int NSLOT = 5;                 // LDS ring of operand slices (2.5 K slices)
     constexpr int QCOLS = WN;                // epilogue pass width: one wave's columns
     constexpr int MW = QCOLS / 32;           // 32-bit words of a pass's candidate mask
     constexpr int SP = QCOLS + 4;            // row pitch (floats) of the epilogue staging
-    constexpr int SMEM = (2 * STAGE > LM_BM * SP * 2) ? 2 * STAGE : LM_BM * SP * 2;
+    constexpr int SMEM = (NSLOT * UNIT > LM_BM * SP * 2) ? NSLOT * UNIT : LM_BM * SP * 2;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
     float* stage = reinterpret_cast<float*>(smem);
 
@@ -178,18 +164,24 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
         (void*)(H + (int64_t)m0 * Hd), (short)0, min(LM_BM, T - m0) * Hd * 2, 0x00020000);
 
     // Per-lane LDS element offsets of the 32 x 16 fragments: row = lane % 32 of
-    // each 32-row block, 16-byte chunk (2 * k16 + lane / 32) ^ (row % 8).
+    // each 32-row block, 16-byte chunk (2 * k16 + lane / 32) ^ swz8(row).
     const int fr = lane & 31;
     const int a_row0 = (wm * 128 + fr) * LM_BK;
-    const int b_row0 = LM_BM * LM_BK + (wn * WN + fr) * LM_BK;
-    int voffA[NIA], voffB[NIB];
-    dma_offsets<NIA>(voffA, wave_s, lane, Hd);
-    dma_offsets<NIB>(voffB, wave_s, lane, Hd);
+    const int b_row0 = (wn * WN + fr) * LM_BK;
 
     for (int nt = n_begin; nt < n_end; ++nt) {
         const int n0 = nt * BN;
         const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(W + (int64_t)n0 * Hd), (short)0, min(BN, V - n0) * Hd * 2, 0x00020000);
+        // LDS-DMA lane offsets, recomputed per tile (from opaque copies of Hd
+        // and the lane, so that they are not hoisted): kept live across the
+        // epilogue they get spilled, and each reload waits for every load in
+        // flight.
+        int hd_t = Hd, lane_t = lane;
+        asm volatile("" : "+s"(hd_t), "+v"(lane_t));
+        int voffA[NIA], voffB[NIB], lcA, lcB;
+        dma_offsets<NIA>(voffA, lcA, wave_s, lane_t, hd_t);
+        dma_offsets<NIB>(voffB, lcB, wave_s, lane_t, hd_t);
         f32x16 acc[MB][NB];
 #pragma unroll
         for (int i = 0; i < MB; ++i)
@@ -198,22 +190,18 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-        auto issue_a = [&](int kt, int st) {
-            dma_slice<NIA>(rsA, smem + st * STAGE, voffA, wave_s, lane, Hd, kt * LM_BK);
-        };
-        auto issue_b = [&](int kt, int st) {
-            dma_slice<NIB>(rsB, smem + st * STAGE + LM_BM * LM_BK, voffB, wave_s, lane, Hd, kt * LM_BK);
-        };
-        // fragments of one 16-wide K step (k16 = 0..3) of the slice in stage st
-        auto read_frags = [&](int st, int k16, bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
-            const uint16_t* base = smem + st * STAGE;
-            const int chs = (((2 * k16 + (lane >> 5)) ^ (lane & 7)) << 3);  // row % 8 == lane % 8
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-                fa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + a_row0 + i * 32 * LM_BK + chs));
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-                fb[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + b_row0 + j * 32 * LM_BK + chs));
+        // Fragment q (in the order the MFMAs below consume them: A0, B0..B{NB-1},
+        // A1..A{MB-1}) of one 16-wide K step (k16 = 0..3) of the slice whose A
+        // and B halves sit in ring slots sa and sb.
+        constexpr int NFR = MB + NB;
+        auto read_frag = [&](int sa, int sb, int k16, int q, bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
+            const int chs = ((2 * k16 + (lane >> 5)) ^ swz8(fr)) << 3;  // swz8(row) == swz8(row % 32)
+            if (q >= 1 && q <= NB)
+                fb[q - 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(smem + sb * UNIT + b_row0 + (q - 1) * 32 * LM_BK + chs));
+            else {
+                const int i = q == 0 ? 0 : q - NB;
+                fa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(smem + sa * UNIT + a_row0 + i * 32 * LM_BK + chs));
+            }
         };
         auto mfmas = [&](const bf16x8 (&fa)[MB], const bf16x8 (&fb)[NB]) {
 #pragma unroll
@@ -222,66 +210,70 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                 for (int j = 0; j < NB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         };
-        // spread the next K step's fragment reads (and NV LDS-DMA loads) between
-        // the MFMAs of the current one
-        constexpr int NG = MB + NB;                  // groups of MFMAs per K step
-        constexpr int MPG = (MB * NB) / NG;          // MFMAs per group
+        // One K step: its MFMAs, with the next step's fragment reads and (for
+        // DMA = 1 / 2) the LDS-DMA loads of an A / B half written between them
+        // in program order.  The order matters: the compiler cannot tell the
+        // DMA's LDS writes from the reads apart, so it keeps them as written,
+        // and the group barriers then spread both between the MFMAs (reads
+        // first, one per MFMA).
+        constexpr int MPK = MB * NB;  // MFMAs per K step
+        auto kstep = [&](const bf16x8 (&fa)[MB], const bf16x8 (&fb)[NB], int ra, int rb, int rk16,
+                         bf16x8 (&na)[MB], bf16x8 (&nb)[NB], int dma, int dkt, int dslot) {
+#pragma unroll
+            for (int q = 0; q < (NFR > NIA ? NFR : NIA); ++q) {
+                if (q < NFR && rk16 >= 0) read_frag(ra, rb, rk16, q, na, nb);
+                if (dma == 1 && q < NIA)
+                    dma_one<NIA, TAIL>(rsA, smem + dslot * UNIT, voffA, lcA, wave_s, hd_t, dkt * LM_BK, q);
+                if (dma == 2 && q < NIB)
+                    dma_one<NIB, TAIL>(rsB, smem + dslot * UNIT, voffB, lcB, wave_s, hd_t, dkt * LM_BK, q);
+            }
+            mfmas(fa, fb);
+#pragma unroll
+            for (int q = 0; q < MPK; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NFR && rk16 >= 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if ((dma == 1 && q < NIA) || (dma == 2 && q < NIB)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        };
 
-        // Software pipeline over 64-wide K slices with two LDS stages and one
-        // barrier per slice.  The fragments of the next 16-wide K step are read
-        // while the MFMAs of the current one run.  The DMA of slice kt+2 goes
-        // into stage kt%2 as soon as the barrier in the last K step of slice kt
-        // shows every wave is done reading it: its A half right after that
-        // barrier, its B half during the first K step of slice kt+1, both spread
-        // between MFMAs.  The wait before that barrier covers slice kt+1.
+        // Software pipeline over 64-wide K slices, one barrier per slice, with
+        // the operand halves of the slices in a ring of five LDS slots: slice k
+        // keeps its B half in slot 2k mod 5 and its A half in slot 2k+1 mod 5.
+        // The barrier at the end of slice k frees its two slots: the A half of
+        // slice k+2 is loaded into one right after it, the B half of slice k+3
+        // into the other during the first K step of slice k+1.  So a B half
+        // (the weight, streamed from HBM) is in flight for about two slices and
+        // an A half (the hidden states, L2/MALL resident) for one.  The wait
+        // before each barrier lets exactly the newest B half stay in flight.
         bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
-        issue_a(0, 0);
-        issue_b(0, 0);
-        if (nK > 1) {
-            issue_a(1, 1);
-            issue_b(1, 1);
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NIA + NIB));  // slice 0 landed, slice 1 may be in flight
-        } else {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        }
+        dma_slice<NIB, TAIL>(rsB, smem + 0 * UNIT, voffB, lcB, wave_s, hd_t, 0);
+        dma_slice<NIA, TAIL>(rsA, smem + 1 * UNIT, voffA, lcA, wave_s, hd_t, 0);
+        dma_slice<NIB, TAIL>(rsB, smem + 2 * UNIT, voffB, lcB, wave_s, hd_t, LM_BK);  // past K: zeros, unused
+        dma_slice<NIA, TAIL>(rsA, smem + 3 * UNIT, voffA, lcA, wave_s, hd_t, LM_BK);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NIB + NIA));  // slice 0 landed
         __builtin_amdgcn_s_barrier();
         compiler_fence();
-        read_frags(0, 0, fa0, fb0);
+        int sb = 0, sa = 1;  // ring slots of the current slice
+#pragma unroll
+        for (int q = 0; q < NFR; ++q) read_frag(sa, sb, 0, q, fa0, fb0);
         for (int kt = 0; kt + 1 < nK; ++kt) {
-            const int st = kt & 1;
-            read_frags(st, 1, fa1, fb1);
-            // B half of slice kt+1 (slice 1 was loaded whole: a harmless repeat)
-            issue_b(kt + 1, st ^ 1);
-            mfmas(fa0, fb0);
-            sched_interleave<NG, MPG, NIB>();
-            read_frags(st, 2, fa0, fb0);
-            mfmas(fa1, fb1);
-            sched_interleave<NG, MPG, 0>();
-            read_frags(st, 3, fa1, fb1);
-            mfmas(fa0, fb0);
-            sched_interleave<NG, MPG, 0>();
-            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): slice kt+1 landed
+            const int sn = sb == 0 ? NSLOT - 1 : sb - 1;  // slot of the B half of slice kt+2
+            kstep(fa0, fb0, sa, sb, 1, fa1, fb1, 2, kt + 2, sn);
+            kstep(fa1, fb1, sa, sb, 2, fa0, fb0, 0, 0, 0);
+            kstep(fa0, fb0, sa, sb, 3, fa1, fb1, 0, 0, 0);
+            // slice kt+1 landed (only the B half of slice kt+2 may still be in flight)
+            __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(NIB));
             __builtin_amdgcn_s_barrier();
             compiler_fence();
-            // A half of slice kt+2 (past the end: range-checked zeros into a dead stage)
-            issue_a(kt + 2, st);
-            read_frags(st ^ 1, 0, fa0, fb0);
-            mfmas(fa1, fb1);
-            sched_interleave<NG, MPG, NIA>();
+            const int sa2 = sb;  // the A half of slice kt+2 goes into the B slot of slice kt
+            sb = sb + 2 >= NSLOT ? sb + 2 - NSLOT : sb + 2;
+            sa = sa + 2 >= NSLOT ? sa + 2 - NSLOT : sa + 2;
+            kstep(fa1, fb1, sa, sb, 0, fa0, fb0, 1, kt + 2, sa2);
         }
-        {
-            const int st = (nK - 1) & 1;
-            read_frags(st, 1, fa1, fb1);
-            mfmas(fa0, fb0);
-            sched_interleave<NG, MPG, 0>();
-            read_frags(st, 2, fa0, fb0);
-            mfmas(fa1, fb1);
-            sched_interleave<NG, MPG, 0>();
-            read_frags(st, 3, fa1, fb1);
-            mfmas(fa0, fb0);
-            sched_interleave<NG, MPG, 0>();
-            mfmas(fa1, fb1);
-        }
+        kstep(fa0, fb0, sa, sb, 1, fa1, fb1, 0, 0, 0);
+        kstep(fa1, fb1, sa, sb, 2, fa0, fb0, 0, 0, 0);
+        kstep(fa0, fb0, sa, sb, 3, fa1, fb1, 0, 0, 0);
+        kstep(fa1, fb1, sa, sb, -1, fa0, fb0, 0, 0, 0);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         compiler_fence();
@@ -507,8 +499,12 @@ template <int BN, int KCAP>
 static void launch_tiles(const LmPlan& p, const uint16_t* H, const uint16_t* W, int T, int V, int Hd,
                          float s, float c, uint64_t* part, hipStream_t st) {
     const float inv_c = c > 0.f ? 1.0f / c : 0.f;
-    hipLaunchKernelGGL((lm_topk_tiles<BN, KCAP>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H, W, T,
-                       V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part);
+    if (Hd % LM_BK == 0)
+        hipLaunchKernelGGL((lm_topk_tiles<BN, KCAP, false>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H, W,
+                           T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part);
+    else
+        hipLaunchKernelGGL((lm_topk_tiles<BN, KCAP, true>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H, W,
+                           T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part);
 }
 
 template <int KCAP>
