@@ -73,6 +73,48 @@ def attn_work(seq_lens, Lq, Hq, Hkv, D, window):
     return nbytes, flops
 
 
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib):
+    """Reduce rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of
+    this benchmark and of --copy-probe-mib to HBM bytes per dflash_lm_topk call
+    (its tile kernel plus its merge), each counter scaled by what it reads for
+    the plain copy of known size, and store them in profiles/traffic.json."""
+    import csv
+
+    def per_kernel(d, counter):
+        out = {}
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    def copy_kib(d, counter):
+        vals = [max(v) for k, v in per_kernel(d, counter).items() if "copyBuffer" in k]
+        return max(vals)
+
+    expect = copy_mib * 1024.0  # KiB the copy reads and writes
+    f_fetch = expect / copy_kib(copy_fetch_dir, "FETCH_SIZE")
+    f_write = expect / copy_kib(copy_write_dir, "WRITE_SIZE")
+
+    def lm_kib(d, counter):
+        tot = 0.0
+        for k, v in per_kernel(d, counter).items():
+            if "lm_topk_tiles" in k or "lm_topk_merge" in k:
+                tot += sum(v) / len(v)
+        return tot
+
+    fetch = lm_kib(fetch_dir, "FETCH_SIZE") * f_fetch * 1024
+    write = lm_kib(write_dir, "WRITE_SIZE") * f_write * 1024
+    rec = {"lm_topk_full": {
+        "source_sha256": hashlib.sha256(open(LM_SOURCE, "rb").read()).hexdigest(),
+        "hbm_bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+        "fetch_scale": f_fetch, "write_scale": f_write,
+        "note": "FETCH_SIZE and WRITE_SIZE per dispatch of the tile and merge kernels (KiB), scaled by "
+                f"the counters' reading for a plain {copy_mib} MiB device copy"}}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def traffic_for(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -87,9 +129,10 @@ def traffic_for(kernel):
     return None
 
 
-def cpu_baseline(cand, attn, edges_per_step, steps_per_sample):
-    """The oracle timed on a bounded sample: 2 candidate-head requests (32 rows)
-    and 1 attention request, i.e. 1/128 of the step's work."""
+def cpu_baseline(cand, attn, edges_per_step, frac):
+    """The oracle timed on a bounded sample of the step: 1/frac of its
+    candidate-head requests and of its attention requests (64 of 256 and 32 of
+    128 at the default 1/4), scaled to a whole step."""
     import numpy as np
     from oracle import dflash_oracle as O
     try:
@@ -98,23 +141,25 @@ def cpu_baseline(cand, attn, edges_per_step, steps_per_sample):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     S, k = cand["steps"], cand["top_k"]
-    rows = np.arange(2 * S)
+    nr = max(1, cand["requests"] // frac)
+    rows = np.arange(nr * S)
     t0 = time.perf_counter()
     ids, vals = O.lm_topk(cand["H"], cand["W"], k, cand["multiplier"], cand["softcap"], rows=rows)
-    O.candidate_edges(cand["P"], cand["S"], ids.reshape(2, S, k), vals.reshape(2, S, k), cand["H"][rows],
-                      cand["Wp"], cand["anchor"][:2])
+    O.candidate_edges(cand["P"], cand["S"], ids.reshape(nr, S, k), vals.reshape(nr, S, k), cand["H"][rows],
+                      cand["Wp"], cand["anchor"][:nr])
     Lq, D = attn["query_len"], attn["head_dim"]
-    q, _, c2 = O.qk_norm_rope_cache(attn["qkv"][:Lq], attn["hq"], attn["hkv"], D, attn["q_w"], attn["k_w"],
-                                    attn["eps"], attn["positions"][:Lq], attn["theta"], attn["slots"][:Lq],
-                                    attn["cache"], attn["block_size"])
-    O.block_attn(q, c2, attn["block_tables"][:1], attn["seq_lens"][:1], Lq, attn["hq"], attn["hkv"], D,
+    na = max(1, attn["requests"] // frac)
+    q, _, c2 = O.qk_norm_rope_cache(attn["qkv"][:na * Lq], attn["hq"], attn["hkv"], D, attn["q_w"], attn["k_w"],
+                                    attn["eps"], attn["positions"][:na * Lq], attn["theta"],
+                                    attn["slots"][:na * Lq], attn["cache"], attn["block_size"])
+    O.block_attn(q, c2, attn["block_tables"][:na], attn["seq_lens"][:na], Lq, attn["hq"], attn["hkv"], D,
                  attn["block_size"], attn["window"], D ** -0.5)
     dt = time.perf_counter() - t0
-    return {"value": edges_per_step / (dt * steps_per_sample), "unit": "edge scores/s", "cores": int(cores),
+    return {"value": edges_per_step / (dt * frac), "unit": "edge scores/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"2 of 256 candidate-head requests (32 rows: LM-head top-k + edges) and 1 of 128 "
-                      f"attention requests (qk-norm/RoPE/cache + attention) = 1/{steps_per_sample} of a step; "
-                      f"{dt:.1f} s on the host, scaled to a whole step"}
+            "sample": f"{nr} of {cand['requests']} candidate-head requests ({nr * S} rows: LM-head top-k + edges) "
+                      f"and {na} of {attn['requests']} attention requests (qk-norm/RoPE/cache + attention) = "
+                      f"1/{frac} of a step; {dt:.1f} s on the host, scaled to a whole step"}
 
 
 def main():
@@ -123,10 +168,17 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=4,
+                    help="the oracle baseline runs 1/N of the step's requests (default 4: about 10-20 s on 16 cores)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times and exit "
                          "(the reference point that scales the HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="reduce rocprofv3 counter directories to profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, copy_mib=1024)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path would shard across GPUs "
               "as described in DESIGN.md but no multi-GPU run is part of this build.", file=sys.stderr)
@@ -284,7 +336,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(cand, attn, edges_per_step, 128)
+        result["cpu_baseline"] = cpu_baseline(cand, attn, edges_per_step, args.cpu_sample)
     print(json.dumps(result), flush=True)
 
 
