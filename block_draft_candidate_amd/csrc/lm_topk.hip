@@ -3,22 +3,23 @@
 // scale = output_multiplier, soft cap = final_logit_softcapping).
 //
 // One pass over the LM-head weight W [V, Hd] computes logit tiles with bf16
-// MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate) and selects top-k in the
+// MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate) and selects top-k in the
 // tile epilogue; the [T, V] logits are never written to HBM.
 //
-//   * A workgroup (256 threads, 4 waves in 2 x 2) owns a 256-row slice of H and
-//     a contiguous run of BN-column tiles of W (its "group").  Each wave
-//     computes a 128 x BN/2 block of a 256 x BN tile; the K loop streams 64-wide
-//     slices of H and W through double-buffered, XOR-swizzled LDS with register
-//     prefetch of the next slice.
+//   * A workgroup (256 threads, 4 waves in 2 x 2, one per SIMD) owns a 256-row
+//     slice of H and a contiguous run of BN-column tiles of W (its "group").
+//     Each wave computes a 128 x BN/2 block of a 256 x BN tile.  The K loop
+//     streams 64-wide slices of H and W with LDS-DMA into a ring of five LDS
+//     slots, so the W half of a slice is in flight for two slices.
 //   * Epilogue: the tile is staged through LDS in two column halves; thread t
 //     scans row t and keeps that row's running top-k of the group in registers
 //     as packed words (ordered bf16 key << 16 | 0xFFFF - column-in-group), so
 //     one unsigned compare orders (key desc, id asc).  A raw-accumulator
 //     threshold derived from the current k-th key skips the scale/softcap work
 //     for almost every column.
-//   * Groups that share W columns are placed on one XCD (workgroup ids go to
-//     XCDs round-robin), so the 256-row slices reuse W through that XCD's L2.
+//   * Row slices and groups are blocked per XCD (workgroup ids go to XCDs
+//     round-robin), so each XCD's L2 serves W tiles to several row slices and
+//     H slices to several groups.
 //   * A merge kernel picks the k best of the groups' partial lists per row.
 #include "common.h"
 
