@@ -32,7 +32,21 @@ METRIC = "edge scores/s + LM-head top-k GB/s as % of HBM peak, 256 reqs×16 step
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-LM_SOURCE = os.path.join(ROOT, "block_draft_candidate_amd", "csrc", "lm_topk.hip")
+LM_SOURCES = [os.path.join(ROOT, "block_draft_candidate_amd", "csrc", f) for f in ("lm_topk.hip", "common.h")]
+
+
+def kernel_fingerprint():
+    """SHA-256 of the LM-head kernel's code (its source and the shared header)
+    with comments and whitespace removed: a comment edit keeps stored counter
+    figures valid, any code change invalidates them."""
+    import re
+    h = hashlib.sha256()
+    for path in LM_SOURCES:
+        src = open(path).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(re.sub(r"\s+", "", src).encode())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -105,7 +119,7 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib
     fetch = lm_kib(fetch_dir, "FETCH_SIZE") * f_fetch * 1024
     write = lm_kib(write_dir, "WRITE_SIZE") * f_write * 1024
     rec = {"lm_topk_full": {
-        "source_sha256": hashlib.sha256(open(LM_SOURCE, "rb").read()).hexdigest(),
+        "code_sha256": kernel_fingerprint(),
         "hbm_bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
         "fetch_scale": f_fetch, "write_scale": f_write,
         "note": "FETCH_SIZE and WRITE_SIZE per dispatch of the tile and merge kernels (KiB), scaled by "
@@ -121,8 +135,7 @@ def traffic_for(kernel):
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel)
-        src = hashlib.sha256(open(LM_SOURCE, "rb").read()).hexdigest()
-        if rec and rec.get("source_sha256") == src:
+        if rec and rec.get("code_sha256") == kernel_fingerprint():
             return rec.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
