@@ -31,6 +31,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source extra flags.  Attention rescales its MFMA accumulators with VALU
+# work every tile; with the default AGPR form they are copied AGPR <-> VGPR
+# around that, so the MFMAs there are kept in their VGPR form.
+EXTRA_FLAGS = {"block_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -46,7 +52,7 @@ def build(verbose: bool = False) -> str:
     try:
         def compile_one(src: str) -> str:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             res = subprocess.run(cmd, capture_output=True, text=True)
             noise = "is not a recognized feature for this target"
             err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)

@@ -7,11 +7,13 @@
 // One workgroup per (request, kv head); wave w handles q head kv * G + w, so the
 // G heads that share a kv head read each K/V tile from HBM once.  A wave's 16
 // MFMA columns are the block's (up to 16) queries.
-//   * K/V tiles of 64 keys (4 cache blocks) go straight from HBM to LDS with
-//     LDS-DMA (global_load_lds_dwordx4), whole 512-byte cache rows (K | V),
-//     double-buffered.  K chunks are XOR-swizzled by row (16-byte units), V
-//     chunks by row (16-byte units, 2 * (row % 8)), so both reads below are
-//     bank-conflict free.
+//   * K/V tiles of 32 keys (2 cache blocks) go straight from HBM to LDS with
+//     LDS-DMA (global_load_lds_dwordx4), whole 512-byte cache rows (K | V), in
+//     a ring of AT_NST stages (AT_NST - 1 tiles in flight).  K chunks are
+//     XOR-swizzled by row (16-byte units), V chunks by row (16-byte units,
+//     2 * (row % 8)), so both reads below are bank-conflict free.  The visible
+//     part of the request's block table is copied to LDS once, so issuing a
+//     tile's loads needs no scalar memory round trip.
 //   * S^T = K Q^T: v_mfma_f32_16x16x32_bf16, K rows from LDS, Q^T from registers;
 //     each lane then holds scores of a single query, so the online softmax
 //     (fp32, exp2) needs only two cross-lane steps.
@@ -25,12 +27,26 @@ namespace dflash {
 
 constexpr int AT_D = 128;
 constexpr int AT_BS = 16;      // cache block size
-constexpr int AT_TK = 64;      // keys per tile
+constexpr int AT_TK = 32;      // keys per tile
+constexpr int AT_NST = 4;      // LDS ring stages (tiles)
+constexpr int AT_BTCAP = 1024; // block-table entries staged in LDS (longer spans read it from HBM)
 constexpr int AT_ROW = 2 * AT_D;  // elements per cache row (K | V)
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 __device__ __forceinline__ void at_fence() { asm volatile("" ::: "memory"); }
+
+// One LDS-DMA instruction: 16 bytes per lane from the cache block at `blk`
+// (one kv head's 16 rows, range-checked to that block) at byte offset `off`,
+// landing at lds + 16 * lane.
+__device__ __forceinline__ void at_load_block_rows(const uint16_t* blk, int off, uint16_t* lds) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, AT_BS * AT_ROW * 2, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+
+// s_waitcnt immediate: vmcnt <= n, lgkmcnt == 0.
+constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
 template <int G>
 __global__ __launch_bounds__(64 * G) void block_attn_kernel(
@@ -38,7 +54,10 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ seq_lens, int Lq,
     int Hq, int Hkv, int window, float scale_log2, uint16_t* __restrict__ out) {
     constexpr int NI = AT_TK / 2 / G;      // LDS-DMA instructions per wave per tile (2 rows each)
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * AT_TK * AT_ROW];
+    static_assert(NI >= 1, "at least one LDS-DMA instruction per wave");
+    // ring of tiles, then the staged block-table entries (one LDS object)
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[AT_NST * AT_TK * AT_ROW + AT_BTCAP * 2];
+    int32_t* const btl = reinterpret_cast<int32_t*>(smem + AT_NST * AT_TK * AT_ROW);
 
     const int r = blockIdx.x / Hkv;
     const int hk = blockIdx.x - r * Hkv;
@@ -63,27 +82,46 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     const int qlo = L - Lq + qi - window + 1;  // lowest visible key of this lane's query
     const int32_t* bt = block_tables + (int64_t)r * max_blocks;
     const int nblk_req = (L + AT_BS - 1) / AT_BS;
+    // cache block of block-table index i (clamped to the request's last block
+    // and to the cache): from LDS when the visible span fits, else from HBM
+    const int blk0 = kstart / AT_BS;
+    const int nvis = nblk_req - blk0;
+    const bool bt_in_lds = nvis <= AT_BTCAP;
+    if (bt_in_lds)
+        for (int i = tid; i < nvis; i += 64 * G) {
+            int b = bt[blk0 + i];
+            btl[i] = b < 0 ? 0 : (b >= num_blocks ? (int)(num_blocks - 1) : b);
+        }
+    __syncthreads();
+    auto block_of = [&](int i) {
+        i = min(i, nblk_req > 0 ? nblk_req - 1 : 0);
+        if (bt_in_lds) return btl[max(i - blk0, 0)];
+        int b = bt[i];
+        return b < 0 ? 0 : (b >= num_blocks ? (int)(num_blocks - 1) : b);
+    };
 
     // DMA lane layout: instruction covers tile rows 2q, 2q+1; lane i -> row 2q + i/32,
     // physical 16-byte chunk i % 32 of the 512-byte row.  Physical chunk pc < 16 holds
     // K chunk pc ^ (row % 16); pc >= 16 holds V chunk (pc - 16) ^ (2 (row % 8)).
+    // Per-lane byte offsets inside a cache block (tile-independent), and per
+    // tile one scalar block base per instruction.
     const int dr = lane >> 5;
     const int pc = lane & 31;
+    int loff[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int rr = (2 * (wave_s * NI + j) + dr) & 15;  // row within the cache block
+        const int lchunk = pc < 16 ? (pc ^ rr) : (16 + ((pc - 16) ^ (2 * (rr & 7))));
+        loff[j] = (rr * AT_ROW + lchunk * 8) * 2;
+    }
     auto issue = [&](int tile, int st) {
         const int kb = kstart + tile * AT_TK;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int qd = wave_s * NI + j;
-            const int row = 2 * qd + dr;            // tile row (key offset)
-            const int blk_i = kb / AT_BS + (2 * qd) / AT_BS;  // uniform per instruction
-            int b = bt[min(blk_i, nblk_req > 0 ? nblk_req - 1 : 0)];
-            b = b < 0 ? 0 : (b >= num_blocks ? (int)(num_blocks - 1) : b);
-            const int rr = row & 15;                // row within the cache block
-            const int lchunk = pc < 16 ? (pc ^ rr) : (16 + ((pc - 16) ^ (2 * (rr & 7))));
-            const uint16_t* src = cache + (((int64_t)b * Hkv + hk) * AT_BS + rr) * AT_ROW + lchunk * 8;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)src,
-                (__attribute__((address_space(3))) void*)(smem + st * AT_TK * AT_ROW + qd * 512), 16, 0, 0);
+            const int b = __builtin_amdgcn_readfirstlane(block_of(kb / AT_BS + (2 * qd) / AT_BS));
+            at_load_block_rows(cache + ((int64_t)b * Hkv + hk) * AT_BS * AT_ROW, loff[j],
+                               smem + st * AT_TK * AT_ROW + qd * 512);
         }
     };
 
@@ -92,21 +130,34 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (ntiles > 0) issue(0, 0);
+#pragma unroll
+    for (int t = 0; t < AT_NST - 1; ++t)
+        if (t < ntiles) issue(t, t);
     for (int tile = 0; tile < ntiles; ++tile) {
-        const int st = tile & 1;
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's DMA of the tile landed
-        __builtin_amdgcn_s_barrier();         // ... and every wave's; stage st^1 is free
+        const int st = tile % AT_NST;
+        // this wave's loads of the tile landed (the later tiles already issued,
+        // up to AT_NST - 2 of them, may still be in flight) ...
+        const int ahead = min(AT_NST - 2, ntiles - 1 - tile);
+        static_assert(AT_NST - 2 <= 2, "wait cases below");
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_lgkm0(2 * NI));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_lgkm0(NI));
+        else __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; the stage of tile - 1 is free
         at_fence();
-        if (tile + 1 < ntiles) issue(tile + 1, st ^ 1);
+        if (tile + AT_NST - 1 < ntiles) issue(tile + AT_NST - 1, (tile + AT_NST - 1) % AT_NST);
         const uint16_t* tb = smem + st * AT_TK * AT_ROW;
         const int kb = kstart + tile * AT_TK;
+        // every key of the tile is visible to every query of the block (the
+        // highest window start is L - window, for the last query), and every
+        // query lane is a real query: no masking
+        const bool interior = Lq == 16 && L >= Lq && kb >= L - window && kb + AT_TK <= L;
 
         // S^T = K Q^T for 4 blocks of 16 keys
-        float sv[4][4];
+        constexpr int NKB = AT_TK / 16;
+        float sv[NKB][4];
         float mt = -INFINITY;
 #pragma unroll
-        for (int kblk = 0; kblk < 4; ++kblk) {
+        for (int kblk = 0; kblk < NKB; ++kblk) {
             f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
             const int row = kblk * 16 + qi;
 #pragma unroll
@@ -115,29 +166,42 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
                 const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(tb + row * AT_ROW + ch * 8));
                 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc, 0, 0, 0);
             }
+            if (interior) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kp = kb + kblk * 16 + 4 * g + e;
-                const bool vis = qvalid && kp < L && kp >= qlo;
-                sv[kblk][e] = vis ? sacc[e] * scale_log2 : -INFINITY;
-                mt = fmaxf(mt, sv[kblk][e]);
+                for (int e = 0; e < 4; ++e) {
+                    sv[kblk][e] = sacc[e] * scale_log2;
+                    mt = fmaxf(mt, sv[kblk][e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kp = kb + kblk * 16 + 4 * g + e;
+                    const bool vis = qvalid && kp < L && kp >= qlo;
+                    sv[kblk][e] = vis ? sacc[e] * scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, sv[kblk][e]);
+                }
             }
         }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mnew = fmaxf(m, mt);
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = exp2f(m - muse);
+        // rescale the running sums only when some query's maximum moved (after
+        // the first tiles it rarely does); v_exp_f32 directly: arguments are
+        // <= 0 and results below 2^-126 may flush to zero
+        if (__ballot(mnew != m) != 0u) {
+            const float alpha = __builtin_amdgcn_exp2f(m - muse);
+            lsum *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+        }
         m = mnew;
-        lsum *= alpha;
+        float pv[NKB][4];
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
-        float pv[4][4];
-#pragma unroll
-        for (int kblk = 0; kblk < 4; ++kblk)
+        for (int kblk = 0; kblk < NKB; ++kblk)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                pv[kblk][e] = exp2f(sv[kblk][e] - muse);
+                pv[kblk][e] = __builtin_amdgcn_exp2f(sv[kblk][e] - muse);
                 lsum += pv[kblk][e];
             }
 
@@ -145,7 +209,7 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
         // element j <-> key 32 s2 + 4 g + j (j < 4) or 32 s2 + 16 + 4 g + (j - 4).
         const int p = lane & 15;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
+        for (int s2 = 0; s2 < AT_TK / 32; ++s2) {
             u32x4 pp;
             pp[0] = pack_bf16x2(pv[2 * s2][0], pv[2 * s2][1]);
             pp[1] = pack_bf16x2(pv[2 * s2][2], pv[2 * s2][3]);
@@ -164,11 +228,8 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
                     (__attribute__((address_space(3))) i16x4*)(tb + o1));
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4*)(tb + o2));
-                u32x4 vv;
-                vv[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-                vv[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-                vv[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-                vv[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+                const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
                 o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), pf, o[mb], 0, 0, 0);
             }
         }
