@@ -47,32 +47,32 @@ __device__ __forceinline__ uint32_t unorder_key(uint32_t o) {
 // tanh through y^15 below |y| = 0.55 (truncation under half an ulp there), and
 // 1 - 2 / (e^{2|y|} + 1) above, where tanh >= 0.5 keeps the subtraction exact
 // enough (hardware exp2 and reciprocal, about 1 ulp each).
+// Both forms are evaluated and one is selected (no divergent branch: this runs
+// once per candidate inside the wave's candidate rounds).
 __device__ __forceinline__ float cap_tanh(float y) {
     const float a = fabsf(y);
-    float t;
-    if (a < 0.55f) {
-        const float z = a * a;
-        float q = -929569.f / 638512875.f;
-        q = fmaf(q, z, 21844.f / 6081075.f);
-        q = fmaf(q, z, -1382.f / 155925.f);
-        q = fmaf(q, z, 62.f / 2835.f);
-        q = fmaf(q, z, -17.f / 315.f);
-        q = fmaf(q, z, 2.f / 15.f);
-        q = fmaf(q, z, -1.f / 3.f);
-        t = fmaf(a * z, q, a);
-    } else {
-        const float e = __builtin_amdgcn_exp2f(a * 2.8853900817779268f);  // e^{2a}; inf for large a
-        t = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
-    }
-    return copysignf(t, y);
+    const float z = a * a;
+    float q = -929569.f / 638512875.f;
+    q = fmaf(q, z, 21844.f / 6081075.f);
+    q = fmaf(q, z, -1382.f / 155925.f);
+    q = fmaf(q, z, 62.f / 2835.f);
+    q = fmaf(q, z, -17.f / 315.f);
+    q = fmaf(q, z, 2.f / 15.f);
+    q = fmaf(q, z, -1.f / 3.f);
+    const float tp = fmaf(a * z, q, a);
+    const float e = __builtin_amdgcn_exp2f(a * 2.8853900817779268f);  // e^{2a}; inf for large a
+    const float te = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+    return copysignf(a < 0.55f ? tp : te, y);
 }
 
 // The top-k key of one accumulator: bf16(c * tanh(s * acc / c)), or bf16(s * acc)
 // without a cap.
 __device__ __forceinline__ uint32_t logit_key_bits(float acc, float s, float c, float inv_c) {
     float x = s * acc;
-    if (c > 0.f) x = c * cap_tanh(x * inv_c);
-    return f32_to_bf16_bits(x);
+    if (c > 0.f) x = c * cap_tanh(x * inv_c);  // c is uniform
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // fp32 -> bf16, round to nearest even
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rne;  // NaN stays a quiet NaN
 }
 
 // A raw-accumulator bound below which a logit's key is certainly smaller than
@@ -340,6 +340,9 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                 }
                 // 1) mask of this row's columns whose raw accumulator reaches the
                 //    threshold (16-byte reads, no divergence)
+                // Bit 31 - j of word w is column 32w + j: each compare's result is
+                // shifted in through the carry (v_cmp + v_addc, two VALU per
+                // column), so the word is built most significant bit first.
                 uint32_t m[MW];
 #pragma unroll
                 for (int w = 0; w < MW; ++w) {
@@ -350,37 +353,38 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int cc = 32 * w + 4 * q + e;
-                            mw |= ((v4[q][e] >= thr && cc < ncols) ? 1u : 0u) << (4 * q + e);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            asm volatile("v_cmp_ge_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+                                         : "+v"(mw) : "v"(v4[q][e]), "v"(thr) : "vcc");
+                    // columns past V (the last tile of the vocabulary) never count
+                    const int valid = min(max(ncols - 32 * w, 0), 32);
+                    if (valid < 32) mw &= valid == 0 ? 0u : ~((1u << (32 - valid)) - 1u);
                     m[w] = mw;
                 }
                 // 2) candidates in column (= token id) order, one per lane per
                 //    round, the LDS read of the next one issued ahead; the
                 //    threshold is raised once per pass, after the rounds.
-                auto pop = [&]() {
+                auto pop = [&]() {  // lowest remaining column (highest bit of the lowest word)
                     int cc = -1;
 #pragma unroll
                     for (int w = MW - 1; w >= 0; --w)
-                        if (m[w]) cc = 32 * w + __builtin_ctz(m[w]);
-                    if (cc >= 0) m[cc >> 5] &= m[cc >> 5] - 1u;
+                        if (m[w]) cc = 32 * w + __builtin_clz(m[w]);
+                    if (cc >= 0) m[cc >> 5] &= ~(0x80000000u >> (cc & 31));
                     return cc;
                 };
                 bool changed = false;
                 int cc = pop();
                 float v = at(cc < 0 ? 0 : cc);
+                // (the threshold does not move inside a pass, so every masked
+                // candidate is evaluated; the insert is a no-op for a key below
+                // the list, and the round body has no branch)
                 while (cc >= 0) {
                     const int cn = pop();
                     const float vn = at(cn < 0 ? 0 : cn);
-                    if (v >= thr) {
-                        const uint32_t kb = logit_key_bits(v, s, c, inv_c);
-                        const uint32_t p = (order_key(kb) << 16) | (0xffffu - (uint32_t)(cbase + cc - gcol0));
-                        if (p > list[KCAP - 1]) {
-                            list_insert(list, p);
-                            changed = true;
-                        }
-                    }
+                    const uint32_t kb = logit_key_bits(v, s, c, inv_c);
+                    const uint32_t p = (order_key(kb) << 16) | (0xffffu - (uint32_t)(cbase + cc - gcol0));
+                    changed |= p > list[KCAP - 1];
+                    list_insert(list, p);
                     cc = cn;
                     v = vn;
                 }
