@@ -98,11 +98,17 @@ __device__ float acc_lower_bound(uint32_t okey, float s, float c) {
 }
 
 // Insert p into the descending list L (the smallest falls off).  A no-op when
-// p <= L[n-1].
+// p <= L[n-1].  With L[j-1] >= L[j], the new L[j] = max(L[j], min(L[j-1], p))
+// is the median of the three: one v_med3_u32 per entry.
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_med3_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
 template <int N>
 __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
 #pragma unroll
-    for (int j = N - 1; j > 0; --j) L[j] = max(L[j], min(L[j - 1], p));
+    for (int j = N - 1; j > 0; --j) L[j] = med3_u32(L[j], L[j - 1], p);
     L[0] = max(L[0], p);
 }
 
