@@ -8,8 +8,8 @@
 // G heads that share a kv head read each K/V tile from HBM once.  A wave's 16
 // MFMA columns are the block's (up to 16) queries.
 //   * K/V tiles of 32 keys (2 cache blocks) go straight from HBM to LDS with
-//     LDS-DMA (global_load_lds_dwordx4), whole 512-byte cache rows (K | V), in
-//     a ring of AT_NST stages (AT_NST - 1 tiles in flight).  K chunks are
+//     LDS-DMA (buffer_load_dwordx4 ... lds), whole 512-byte cache rows (K | V),
+//     in a ring of AT_NST stages (AT_NST - 1 tiles in flight).  K chunks are
 //     XOR-swizzled by row (16-byte units), V chunks by row (16-byte units,
 //     2 * (row % 8)), so both reads below are bank-conflict free.  The visible
 //     part of the request's block table is copied to LDS once, so issuing a
@@ -28,7 +28,9 @@ namespace dflash {
 constexpr int AT_D = 128;
 constexpr int AT_BS = 16;      // cache block size
 constexpr int AT_TK = 32;      // keys per tile
-constexpr int AT_NST = 4;      // LDS ring stages (tiles)
+constexpr int AT_NST = 2;      // LDS ring stages (tiles): 36 KB of LDS per workgroup lets four
+                               // workgroups share a CU, which hides more than deeper rings with
+                               // fewer workgroups (measured: 2 stages 194 us, 3: 256, 4: 251, 8: 409)
 constexpr int AT_BTCAP = 1024; // block-table entries staged in LDS (longer spans read it from HBM)
 constexpr int AT_ROW = 2 * AT_D;  // elements per cache row (K | V)
 
@@ -47,6 +49,18 @@ __device__ __forceinline__ void at_load_block_rows(const uint16_t* blk, int off,
 
 // s_waitcnt immediate: vmcnt <= n, lgkmcnt == 0.
 constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Wait until at most `ahead` tiles of NI loads each are still in flight
+// (ahead in [0, MAXA]; the immediate must be a constant, hence the cases).
+template <int MAXA, int NI>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+    if constexpr (MAXA <= 0) {
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
+    } else {
+        if (ahead >= MAXA) __builtin_amdgcn_s_waitcnt(vm_lgkm0(MAXA * NI));
+        else wait_tiles_ahead<MAXA - 1, NI>(ahead);
+    }
+}
 
 template <int G>
 __global__ __launch_bounds__(64 * G) void block_attn_kernel(
@@ -138,10 +152,7 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
         // this wave's loads of the tile landed (the later tiles already issued,
         // up to AT_NST - 2 of them, may still be in flight) ...
         const int ahead = min(AT_NST - 2, ntiles - 1 - tile);
-        static_assert(AT_NST - 2 <= 2, "wait cases below");
-        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_lgkm0(2 * NI));
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_lgkm0(NI));
-        else __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
+        wait_tiles_ahead<AT_NST - 2, NI>(ahead);
         __builtin_amdgcn_s_barrier();  // ... and every wave's; the stage of tile - 1 is free
         at_fence();
         if (tile + AT_NST - 1 < ntiles) issue(tile + AT_NST - 1, (tile + AT_NST - 1) % AT_NST);
