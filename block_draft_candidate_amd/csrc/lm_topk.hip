@@ -462,6 +462,56 @@ __global__ __launch_bounds__(256) void lm_topk_merge(const uint64_t* __restrict_
     }
 }
 
+// Merge for G <= 16 groups: 16 lanes per row (four rows per wave), lane g
+// holding group g's sorted list in registers.  Each round takes the largest
+// head over the 16 lanes (DPP row rotations, no LDS round trip) and the lane
+// that owns it (entries are distinct; 0 = empty) drops it.
+template <int SH>
+__device__ __forceinline__ uint64_t max_ror(uint64_t x) {
+    constexpr int ctrl = 0x120 + SH;  // DPP row_ror:SH (rotate within each 16-lane row)
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, ctrl, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), ctrl, 0xF, 0xF, false);
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    return y > x ? y : x;
+}
+__device__ __forceinline__ uint64_t row16_max(uint64_t x) {
+    return max_ror<8>(max_ror<4>(max_ror<2>(max_ror<1>(x))));
+}
+
+template <int KCAP>
+__global__ __launch_bounds__(256) void lm_topk_merge16(const uint64_t* __restrict__ part, int T, int G, int k,
+                                                       int32_t* __restrict__ ids, float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const int g = lane & 15;
+    uint64_t L[KCAP];
+    if (row < T && g < G) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(part + ((int64_t)row * G + g) * KCAP);
+#pragma unroll
+        for (int j = 0; j < KCAP / 2; ++j) {
+            const u32x4 v = src[j];
+            L[2 * j] = ((uint64_t)v[1] << 32) | v[0];
+            L[2 * j + 1] = ((uint64_t)v[3] << 32) | v[2];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KCAP; ++j) L[j] = 0;
+    }
+    for (int r = 0; r < k; ++r) {
+        const uint64_t best = row16_max(L[0]);
+        if (best != 0 && L[0] == best) {
+#pragma unroll
+            for (int j = 0; j < KCAP - 1; ++j) L[j] = L[j + 1];
+            L[KCAP - 1] = 0;
+        }
+        if (g == 0 && row < T) {
+            const uint32_t okey = (uint32_t)(best >> 32);
+            ids[(int64_t)row * k + r] = (int32_t)(~(uint32_t)best);
+            logits[(int64_t)row * k + r] = best ? bf16_bits_to_f32(unorder_key(okey)) : -INFINITY;
+        }
+    }
+}
+
 struct LmPlan {
     int BN, KCAP, nM, nN, G, xmx;
     int64_t nwg;
@@ -525,8 +575,12 @@ static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, in
         launch_tiles<256, KCAP>(p, H, W, T, V, Hd, s, c, part, st);
     else
         launch_tiles<128, KCAP>(p, H, W, T, V, Hd, s, c, part, st);
-    hipLaunchKernelGGL((lm_topk_merge<KCAP>), dim3((T + 3) / 4), dim3(256), 0, st, part, T, p.G, k, ids,
-                       logits);
+    if (p.G <= 16)
+        hipLaunchKernelGGL((lm_topk_merge16<KCAP>), dim3((T + 15) / 16), dim3(256), 0, st, part, T, p.G, k, ids,
+                           logits);
+    else
+        hipLaunchKernelGGL((lm_topk_merge<KCAP>), dim3((T + 3) / 4), dim3(256), 0, st, part, T, p.G, k, ids,
+                           logits);
 }
 
 }  // namespace dflash

@@ -3,64 +3,47 @@
 // weights, the rope's cos/sin cache and, when the cache is bf16, the layer's
 // kv cache and slot mapping).
 //
-// Sixteen lanes own one head (head_dim 128 = 16 lanes x 8 bf16, one 16-byte
-// load and store per lane); a 256-thread workgroup handles 16 heads.  The sum of
-// squares is reduced inside the 16-lane group, and the RoPE partner (i <-> i +
-// 64) of a lane's 8 elements lives in lane ^ 8 of the same group.  V heads are
-// copied to the cache bit for bit.
+// One workgroup per token.  Sixteen lanes own one head (head_dim 128 = 16
+// lanes x 8 bf16, one 16-byte load and store per lane); the 16 groups of a
+// 256-thread workgroup take heads g, g + 16, ...  The token's position, slot,
+// RoPE row and every head's data are loaded up front, so a workgroup pays one
+// memory round trip (plus the position -> RoPE row step).  The sum of squares is
+// reduced inside the 16-lane group, and the RoPE partner (i <-> i + 64) of a
+// lane's 8 elements lives in lane ^ 8 of the same group.  V heads are copied to
+// the cache bit for bit.
 #include "common.h"
 
 namespace dflash {
 
 constexpr int QK_D = 128;
+constexpr int QK_HPG = 4;  // heads per 16-lane group handled per round (48 heads: 3 used)
 
 __global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
-    const uint16_t* __restrict__ qkv, int64_t row_stride, int64_t n_items, int Hq, int Hkv,
+    const uint16_t* __restrict__ qkv, int64_t row_stride, int Hq, int Hkv,
     const uint16_t* __restrict__ q_w, const uint16_t* __restrict__ k_w, float eps,
     const int64_t* __restrict__ positions, const float* __restrict__ cos_sin, int64_t max_pos,
     const int64_t* __restrict__ slots, uint16_t* __restrict__ cache, int64_t num_blocks, int block_size,
     uint16_t* __restrict__ q_out, uint16_t* __restrict__ k_out) {
     const int NH = Hq + 2 * Hkv;
-    const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    if (item >= n_items) return;
-    const int64_t t = item / NH;
-    const int h = (int)(item - t * NH);
+    const int64_t t = blockIdx.x;
+    const int grp = threadIdx.x >> 4;
     const int j = threadIdx.x & 15;
-
-    const u32x4 raw = ldg16(qkv + t * row_stride + (int64_t)h * QK_D + j * 8);
-
-    int64_t cache_row = -1;  // element offset of [blk, head, off, 0] in the cache
-    if (cache != nullptr && h >= Hq) {
-        const int64_t s = slots[t];
-        if (s >= 0 && s < num_blocks * block_size) {
-            const int64_t blk = s / block_size, off = s - blk * block_size;
-            const int hk = (h >= Hq + Hkv) ? h - Hq - Hkv : h - Hq;
-            cache_row = ((blk * Hkv + hk) * block_size + off) * (2 * QK_D);
-        }
-    }
-    if (h >= Hq + Hkv) {  // v head: copied as is
-        if (cache_row >= 0) stg16(cache + cache_row + QK_D + j * 8, raw);
-        return;
-    }
-
-    float x[8];
-    unpack8(raw, x);
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 16);
-    const float rinv = 1.0f / sqrtf(ss * (1.0f / QK_D) + eps);
-
-    const bool is_q = h < Hq;
-    float w[8];
-    unpack8(ldg16((is_q ? q_w : k_w) + j * 8), w);
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = x[e] * rinv * w[e];
+    const uint16_t* row = qkv + t * row_stride + j * 8;
 
     int64_t pos = positions[t];
     pos = pos < 0 ? 0 : (pos >= max_pos ? max_pos - 1 : pos);
+    int64_t cache_base = -1;  // element offset of [blk, 0, off, 0] in the cache
+    if (cache != nullptr) {
+        const int64_t s = slots[t];
+        if (s >= 0 && s < num_blocks * block_size) {
+            const int64_t blk = s / block_size, off = s - blk * block_size;
+            cache_base = (blk * Hkv * block_size + off) * (2 * QK_D);
+        }
+    }
+    const int64_t head_stride = (int64_t)block_size * 2 * QK_D;  // next kv head of the same block
+    float qw[8], kw[8];
+    unpack8(ldg16(q_w + j * 8), qw);
+    unpack8(ldg16(k_w + j * 8), kw);
     const float* cs = cos_sin + pos * QK_D + (j & 7) * 8;
     const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
     const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
@@ -68,23 +51,52 @@ __global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
     const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + QK_D / 2 + 4);
     const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
     const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float partner = __shfl_xor(y[e], 8, 16);
-        // first half: x1 cos - x2 sin;  second half: x2 cos + x1 sin
-        o[e] = (j < 8) ? (y[e] * cv[e] - partner * sv[e]) : (y[e] * cv[e] + partner * sv[e]);
-    }
-    u32x4 packed;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) packed[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
 
-    if (is_q) {
-        stg16(q_out + (t * Hq + h) * QK_D + j * 8, packed);
-    } else {
-        const int hk = h - Hq;
-        if (k_out != nullptr) stg16(k_out + (t * Hkv + hk) * QK_D + j * 8, packed);
-        if (cache_row >= 0) stg16(cache + cache_row + j * 8, packed);
+    for (int h0 = grp; h0 < NH; h0 += 16 * QK_HPG) {
+        u32x4 raw[QK_HPG];
+#pragma unroll
+        for (int i = 0; i < QK_HPG; ++i) {
+            const int h = h0 + 16 * i;
+            raw[i] = h < NH ? ldg16(row + (int64_t)h * QK_D) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < QK_HPG; ++i) {
+            const int h = h0 + 16 * i;
+            if (h >= NH) break;  // uniform within the 16-lane group
+            if (h >= Hq + Hkv) {  // v head: copied as is
+                if (cache_base >= 0) stg16(cache + cache_base + (h - Hq - Hkv) * head_stride + QK_D + j * 8, raw[i]);
+                continue;
+            }
+            float x[8];
+            unpack8(raw[i], x);
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 16);
+            const float rinv = 1.0f / sqrtf(ss * (1.0f / QK_D) + eps);
+            const bool is_q = h < Hq;
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = x[e] * rinv * (is_q ? qw[e] : kw[e]);
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float partner = __shfl_xor(y[e], 8, 16);
+                // first half: x1 cos - x2 sin;  second half: x2 cos + x1 sin
+                o[e] = (j < 8) ? (y[e] * cv[e] - partner * sv[e]) : (y[e] * cv[e] + partner * sv[e]);
+            }
+            u32x4 packed;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) packed[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+            if (is_q) {
+                stg16(q_out + (t * Hq + h) * QK_D + j * 8, packed);
+            } else {
+                const int hk = h - Hq;
+                if (k_out != nullptr) stg16(k_out + (t * Hkv + hk) * QK_D + j * 8, packed);
+                if (cache_base >= 0) stg16(cache + cache_base + hk * head_stride + j * 8, packed);
+            }
+        }
     }
 }
 
@@ -132,11 +144,10 @@ extern "C" int dflash_qk_norm_rope_cache(const uint16_t* qkv, int64_t row_stride
     if (T_q < 1 || Hq < 1 || Hkv < 1 || max_pos < 1 || !(eps >= 0.f)) return DFLASH_ERR_INVALID_ARG;
     if (D != QK_D) return DFLASH_ERR_UNSUPPORTED;
     if (row_stride < (int64_t)(Hq + 2 * Hkv) * D || row_stride % 8 != 0) return DFLASH_ERR_INVALID_ARG;
-    const int64_t n_items = T_q * (int64_t)(Hq + 2 * Hkv);
-    if (n_items / 16 + 1 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(qk_norm_rope_cache_kernel, dim3((unsigned)((n_items + 15) / 16)), dim3(256), 0,
-                       reinterpret_cast<hipStream_t>(stream), qkv, row_stride, n_items, Hq, Hkv, q_w, k_w,
-                       eps, positions, cos_sin, max_pos, slots, kv_cache, num_blocks, block_size, q_out, k_out);
+    if (T_q > INT32_MAX || (int64_t)Hq + 2 * (int64_t)Hkv > 65536) return DFLASH_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(qk_norm_rope_cache_kernel, dim3((unsigned)T_q), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), qkv, row_stride, Hq, Hkv, q_w, k_w, eps, positions,
+                       cos_sin, max_pos, slots, kv_cache, num_blocks, block_size, q_out, k_out);
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
 }
