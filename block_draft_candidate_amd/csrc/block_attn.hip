@@ -47,21 +47,6 @@ __device__ __forceinline__ void at_load_block_rows(const uint16_t* blk, int off,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 
-// s_waitcnt immediate: vmcnt <= n, lgkmcnt == 0.
-constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
-
-// Wait until at most `ahead` tiles of NI loads each are still in flight
-// (ahead in [0, MAXA]; the immediate must be a constant, hence the cases).
-template <int MAXA, int NI>
-__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
-    if constexpr (MAXA <= 0) {
-        __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
-    } else {
-        if (ahead >= MAXA) __builtin_amdgcn_s_waitcnt(vm_lgkm0(MAXA * NI));
-        else wait_tiles_ahead<MAXA - 1, NI>(ahead);
-    }
-}
-
 template <int G>
 __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ cache, int64_t num_blocks,
@@ -152,7 +137,7 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
         // this wave's loads of the tile landed (the later tiles already issued,
         // up to AT_NST - 2 of them, may still be in flight) ...
         const int ahead = min(AT_NST - 2, ntiles - 1 - tile);
-        wait_tiles_ahead<AT_NST - 2, NI>(ahead);
+        wait_stages_ahead<AT_NST - 2, NI>(ahead);
         __builtin_amdgcn_s_barrier();  // ... and every wave's; the stage of tile - 1 is free
         at_fence();
         if (tile + AT_NST - 1 < ntiles) issue(tile + AT_NST - 1, (tile + AT_NST - 1) % AT_NST);

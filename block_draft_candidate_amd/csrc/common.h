@@ -117,6 +117,22 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
+// s_waitcnt immediate that waits for vmcnt <= n and lgkmcnt == 0.
+constexpr int vm_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Wait until at most `ahead` ring stages of NI loads each are still in flight
+// (and lgkmcnt == 0); ahead is clamped to [0, MAXA].  The immediate must be a
+// constant, hence the cases.
+template <int MAXA, int NI>
+__device__ __forceinline__ void wait_stages_ahead(int ahead) {
+    if constexpr (MAXA <= 0) {
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+    } else {
+        if (ahead >= MAXA) __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(MAXA * NI));
+        else wait_stages_ahead<MAXA - 1, NI>(ahead);
+    }
+}
+
 }  // namespace dflash
 
 // Host-side helpers shared by the entry points.

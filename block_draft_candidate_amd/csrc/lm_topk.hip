@@ -112,9 +112,6 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
     L[0] = max(L[0], p);
 }
 
-// s_waitcnt immediate that waits for vmcnt <= n and lgkmcnt == 0.
-constexpr int vm_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
-
 template <int BN, int KCAP, bool TAIL>
 __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ W, int T, int V, int Hd,

@@ -102,7 +102,7 @@ int dflash_lm_topk(const uint16_t* H, const uint16_t* W,
  *   ws                dflash_candidate_edges_workspace_size(Rq*S, R, Hd) bytes
  *
  * Requirements: Rq, S, V >= 1; 1 <= k <= min(V, 64); R % 16 == 0, 16 <= R <= 256;
- * Hd % 8 == 0.  Ids and anchors outside [0, V) are clamped into range.
+ * Hd % 8 == 0, Hd <= 2^22.  Ids and anchors outside [0, V) are clamped into range.
  * Deterministic; edges[r, 0, q, :] is bit-identical for every q.
  * ---------------------------------------------------------------------- */
 size_t dflash_candidate_edges_workspace_size(int64_t T, int32_t R, int64_t Hd);
