@@ -2,12 +2,16 @@
 """Benchmark of the DFlash2 block-draft candidate step on one MI355X.
 
 One step = the whole hot path over one synthetic batch, inputs resident in HBM:
-  1. dflash_lm_topk            256 requests x 16 steps, vocab 151936, hidden 4096, top_k 16,
-                               output_multiplier 0.5, softcap 30
-  2. dflash_candidate_edges    the same rows, rank 128, on step 1's ids and logits
+  1. dflash_lm_topk_proj       256 requests x 16 steps, vocab 151936, hidden 4096, top_k 16,
+                               output_multiplier 0.5, softcap 30, and the selector's rank-128
+                               projection of the same hidden states in the same pass
+  2. dflash_candidate_edges_hp edge scores of the same rows from step 1's ids, logits and
+                               projection
   3. dflash_qk_norm_rope_cache draft-layer query block, 128 requests x 16 tokens, 32/8 heads
   4. dflash_block_attn         the same block over the paged cache, window 2048,
                                context lengths uniform in [512, 8192]
+With --two-kernel-edges, steps 1-2 are dflash_lm_topk and dflash_candidate_edges
+(projection and edges in their own two kernels).
 
 Prints one JSON line.  `value` is edge scores per second of the whole step.
 Per-kernel times come from HIP events on the stream the kernels run on; the
@@ -53,18 +57,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def lm_bytes(T, V, Hd, k):
-    return V * Hd * 2 + T * Hd * 2 + T * k * 8
+def lm_bytes(T, V, Hd, k, R=0):
+    """W, H, ids + logits; with the rank projection (R > 0) also W_proj and hp."""
+    return V * Hd * 2 + T * Hd * 2 + T * k * 8 + R * Hd * 2 + T * R * 4
 
 
-def lm_flops(T, V, Hd):
-    return 2 * T * V * Hd
+def lm_flops(T, V, Hd, R=0):
+    return 2 * T * (V + R) * Hd
 
 
-def edge_bytes(Rq, S, k, R, Hd):
+def edge_bytes(Rq, S, k, R, Hd, from_hp=False):
+    """Gathered codebook rows, ids, unary logits, anchors, edges, and either H +
+    W_proj (projection inside) or hp (given)."""
     T = Rq * S
     gathers = Rq * (1 + (S - 1) * k) * R * 2 + Rq * S * k * R * 2
-    return T * Hd * 2 + R * Hd * 2 + gathers + T * k * 4 * 2 + Rq * 4 + T * k * k * 4
+    proj = T * R * 4 if from_hp else T * Hd * 2 + R * Hd * 2
+    return proj + gathers + T * k * 4 * 2 + Rq * 4 + T * k * k * 4
 
 
 def qk_bytes(Tq, Hq, Hkv, D):
@@ -87,11 +95,13 @@ def attn_work(seq_lens, Lq, Hq, Hkv, D, window):
     return nbytes, flops
 
 
-def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib):
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, key):
     """Reduce rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of
-    this benchmark and of --copy-probe-mib to HBM bytes per dflash_lm_topk call
-    (its tile kernel plus its merge), each counter scaled by what it reads for
-    the plain copy of known size, and store them in profiles/traffic.json."""
+    this benchmark and of --copy-probe-mib to HBM bytes per LM-head call (its
+    tile kernel plus its merge), each counter scaled by what it reads for the
+    plain copy of known size, and store them under `key` in
+    profiles/traffic.json (lm_topk_proj_full: the benchmark's default path,
+    lm_topk_full: --two-kernel-edges)."""
     import csv
 
     def per_kernel(d, counter):
@@ -118,12 +128,17 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib
 
     fetch = lm_kib(fetch_dir, "FETCH_SIZE") * f_fetch * 1024
     write = lm_kib(write_dir, "WRITE_SIZE") * f_write * 1024
-    rec = {"lm_topk_full": {
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[key] = {
         "code_sha256": kernel_fingerprint(),
         "hbm_bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
         "fetch_scale": f_fetch, "write_scale": f_write,
         "note": "FETCH_SIZE and WRITE_SIZE per dispatch of the tile and merge kernels (KiB), scaled by "
-                f"the counters' reading for a plain {copy_mib} MiB device copy"}}
+                f"the counters' reading for a plain {copy_mib} MiB device copy"}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -181,6 +196,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-kernel-edges", action="store_true",
+                    help="LM head and edges as dflash_lm_topk + dflash_candidate_edges (projection in the edge "
+                         "call) instead of dflash_lm_topk_proj + dflash_candidate_edges_hp")
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="the oracle baseline runs 1/N of the step's requests (default 4: about 10-20 s on 16 cores)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -190,7 +208,8 @@ def main():
                     help="reduce rocprofv3 counter directories to profiles/traffic.json and exit")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic, copy_mib=1024)
+        write_traffic(*args.write_traffic, copy_mib=1024,
+                      key="lm_topk_full" if args.two_kernel_edges else "lm_topk_proj_full")
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path would shard across GPUs "
@@ -232,6 +251,8 @@ def main():
     edges = torch.empty((Rq, S, k, k), dtype=torch.float32, device=dev)
     ws_lm = torch.empty(B.lm_topk_workspace_size(T, V, Hd, k), dtype=torch.uint8, device=dev)
     ws_e = torch.empty(B.candidate_edges_workspace_size(T, R, Hd), dtype=torch.uint8, device=dev)
+    hp = torch.empty((T, R), dtype=torch.float32, device=dev)
+    fused = not args.two_kernel_edges
 
     Lq, Hq, Hkv, D = attn["query_len"], attn["hq"], attn["hkv"], attn["head_dim"]
     Rq_a = attn["requests"]
@@ -258,9 +279,15 @@ def main():
             fn()
             if timed:
                 ev[n][1].record()
-        call("lm_topk", lambda: B.lm_topk(H, W, k, cand["multiplier"], cand["softcap"], ids, logits, ws_lm))
-        call("edges", lambda: B.candidate_edges(P, Sc, ids.view(Rq, S, k), logits.view(Rq, S, k), H, Wp, anchor,
-                                                edges, ws_e))
+        if fused:
+            call("lm_topk", lambda: B.lm_topk_proj(H, W, k, cand["multiplier"], cand["softcap"], Wp, ids, logits,
+                                                   hp, ws_lm))
+            call("edges", lambda: B.candidate_edges_hp(P, Sc, ids.view(Rq, S, k), logits.view(Rq, S, k), hp,
+                                                       anchor, edges))
+        else:
+            call("lm_topk", lambda: B.lm_topk(H, W, k, cand["multiplier"], cand["softcap"], ids, logits, ws_lm))
+            call("edges", lambda: B.candidate_edges(P, Sc, ids.view(Rq, S, k), logits.view(Rq, S, k), H, Wp,
+                                                    anchor, edges, ws_e))
         call("qk", lambda: B.qk_norm_rope_cache(qkv, Hq, Hkv, D, q_w, k_w, attn["eps"], positions, cos_sin,
                                                 slots, cache, q_out=q_out, want_k=False))
         call("attn", lambda: B.block_attn(q_out, cache, tables, seq_lens, Lq, attn["window"], out=a_out))
@@ -292,8 +319,9 @@ def main():
     edges_per_step = Rq * S * k * k
     value = edges_per_step / (ms_per_step / 1e3)
 
-    lmb, lmf = lm_bytes(T, V, Hd, k), lm_flops(T, V, Hd)
-    eb = edge_bytes(Rq, S, k, R, Hd)
+    Rp = R if fused else 0
+    lmb, lmf = lm_bytes(T, V, Hd, k, Rp), lm_flops(T, V, Hd, Rp)
+    eb = edge_bytes(Rq, S, k, R, Hd, from_hp=fused)
     qb = qk_bytes(Rq_a * Lq, Hq, Hkv, D)
     ab, af = attn_work(attn["seq_lens"], Lq, Hq, Hkv, D, attn["window"])
     lm_tflops = lmf / (kms["lm_topk"] * 1e-3) / 1e12
@@ -320,15 +348,19 @@ def main():
             "requests": Rq, "steps": S, "top_k": k, "vocab": V, "hidden": Hd, "rank": R,
             "attn_requests": Rq_a, "attn_queries": Lq, "heads": [Hq, Hkv], "head_dim": D,
             "window": attn["window"],
+            "lm_head_and_edges": ("dflash_lm_topk_proj (rank projection in the LM-head pass) + "
+                                  "dflash_candidate_edges_hp" if fused else
+                                  "dflash_lm_topk + dflash_candidate_edges (projection in the edge call)"),
         },
         "roofline": {
-            "kernel": "dflash_lm_topk (tile GEMM + top-k, and its merge)",
+            "kernel": ("dflash_lm_topk_proj (tile GEMM + top-k + rank projection, and its merge)" if fused
+                       else "dflash_lm_topk (tile GEMM + top-k, and its merge)"),
             "bound": "mfma",
             "achieved": lm_tflops,
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": lm_tflops / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": traffic_for("lm_topk_full"),
+            "traffic": traffic_for("lm_topk_proj_full" if fused else "lm_topk_full"),
         },
         "kernels": {
             "lm_topk": {"ms": kms["lm_topk"], "GB_per_s": lm_gbs, "hbm_frac": lm_gbs / HBM_PEAK_GBS,

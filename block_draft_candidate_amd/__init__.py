@@ -13,8 +13,8 @@ import os
 import torch
 
 __all__ = [
-    "DFlashError", "lib", "lm_topk", "lm_topk_workspace_size", "candidate_edges",
-    "candidate_edges_workspace_size", "rope_cos_sin", "qk_norm_rope_cache", "block_attn",
+    "DFlashError", "lib", "lm_topk", "lm_topk_workspace_size", "lm_topk_proj", "candidate_edges",
+    "candidate_edges_workspace_size", "candidate_edges_hp", "rope_cos_sin", "qk_norm_rope_cache", "block_attn",
     "LIB_PATH",
 ]
 
@@ -29,7 +29,11 @@ _SIGS = {
     "dflash_lm_topk_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32]),
     "dflash_lm_topk": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32,
                                       _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "dflash_lm_topk_proj": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32,
+                                           _c_p, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dflash_candidate_edges_workspace_size": (_c_sz, [_c_i64, _c_i32, _c_i64]),
+    "dflash_candidate_edges_hp": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32,
+                                                 _c_i64, _c_i32, _c_p, _c_p]),
     "dflash_candidate_edges": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32,
                                               _c_i32, _c_i64, _c_i32, _c_i64, _c_p, _c_p, _c_sz, _c_p]),
     "dflash_rope_cos_sin": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_f64, _c_p]),
@@ -120,6 +124,31 @@ def lm_topk(H: torch.Tensor, W: torch.Tensor, k: int, output_multiplier: float =
     return ids, logits
 
 
+def lm_topk_proj(H: torch.Tensor, W: torch.Tensor, k: int, output_multiplier: float, softcap: float,
+                 W_proj: torch.Tensor, ids: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                 hp: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """``lm_topk`` plus the rank projection ``hp = H . W_proj^T`` (fp32 [T, R])
+    from the same pass over H.  Returns ``(ids, logits, hp)``."""
+    T, Hd = H.shape
+    V = W.shape[0]
+    R = W_proj.shape[0]
+    if W.shape[1] != Hd or W_proj.shape[1] != Hd:
+        raise ValueError("H, W and W_proj disagree on the hidden size")
+    dev = H.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    logits = torch.empty((T, k), dtype=torch.float32, device=dev) if logits is None else logits
+    hp = torch.empty((T, R), dtype=torch.float32, device=dev) if hp is None else hp
+    ws = _workspace(lm_topk_workspace_size(T, V, Hd, k), dev, workspace)
+    st = lib().dflash_lm_topk_proj(_dev(H, torch.bfloat16, "H"), _dev(W, torch.bfloat16, "W"), T, V, Hd, k,
+                                   float(output_multiplier), float(softcap),
+                                   _dev(W_proj, torch.bfloat16, "W_proj"), R,
+                                   _dev(ids, torch.int32, "ids"), _dev(logits, torch.float32, "logits"),
+                                   _dev(hp, torch.float32, "hp"),
+                                   ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dflash_lm_topk_proj")
+    return ids, logits, hp
+
+
 # ---------------------------------------------------------------- edge scores
 def candidate_edges_workspace_size(T: int, R: int, Hd: int) -> int:
     return int(lib().dflash_candidate_edges_workspace_size(T, R, Hd))
@@ -147,6 +176,26 @@ def candidate_edges(pred_cb, succ_cb, cand_ids, unary, H, W_proj, anchor,
         _dev(out, torch.float32, "out"), ws.data_ptr(), ws.numel() * ws.element_size(),
         _stream(stream))
     _check(st, "dflash_candidate_edges")
+    return out
+
+
+def candidate_edges_hp(pred_cb, succ_cb, cand_ids, unary, hp, anchor, out: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """Edge scores ``[Rq, S, k, k]`` (fp32) from a given projection ``hp``
+    (fp32 [Rq*S, R], e.g. from ``lm_topk_proj``)."""
+    Rq, S, k = cand_ids.shape
+    V, R = pred_cb.shape
+    if succ_cb.shape != (V, R) or hp.shape != (Rq * S, R):
+        raise ValueError("shape mismatch between codebooks and projection")
+    if unary.shape != (Rq, S, k) or anchor.shape != (Rq,):
+        raise ValueError("unary must be [Rq, S, k] and anchor [Rq]")
+    out = torch.empty((Rq, S, k, k), dtype=torch.float32, device=hp.device) if out is None else out
+    st = lib().dflash_candidate_edges_hp(
+        _dev(pred_cb, torch.bfloat16, "pred_cb"), _dev(succ_cb, torch.bfloat16, "succ_cb"),
+        _dev(cand_ids, torch.int32, "cand_ids"), _dev(unary, torch.float32, "unary"),
+        _dev(hp, torch.float32, "hp"), _dev(anchor, torch.int32, "anchor"), Rq, S, k, V, R,
+        _dev(out, torch.float32, "out"), _stream(stream))
+    _check(st, "dflash_candidate_edges_hp")
     return out
 
 

@@ -468,3 +468,30 @@ extern "C" int dflash_candidate_edges(const uint16_t* pred_cb, const uint16_t* s
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
 }
+
+extern "C" int dflash_candidate_edges_hp(const uint16_t* pred_cb, const uint16_t* succ_cb,
+                                         const int32_t* cand_ids, const float* unary, const float* hp,
+                                         const int32_t* anchor, int64_t Rq, int32_t S, int32_t k, int64_t V,
+                                         int32_t R, float* edges, void* stream) {
+    const void* ptrs[] = {pred_cb, succ_cb, cand_ids, unary, hp, anchor, edges};
+    for (const void* q : ptrs)
+        if (!q || !DFLASH_ALIGNED16(q)) return DFLASH_ERR_INVALID_ARG;
+    if (Rq < 1 || S < 1 || V < 1 || k < 1 || k > V || R < 1) return DFLASH_ERR_INVALID_ARG;
+    if (k > 64 || R % 16 != 0 || R > 256) return DFLASH_ERR_UNSUPPORTED;
+    const int64_t T = Rq * (int64_t)S;
+    if (T > INT32_MAX / 64 || V > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int Ti = (int)T;
+    const int KB = (k + 15) / 16;
+    bool ok;
+    // h_p given: the bilinear stage alone, on one "partial"
+    if (KB == 1)
+        ok = launch_bilinear<1>(pred_cb, succ_cb, cand_ids, unary, hp, 1, anchor, Ti, S, k, (int)V, R, edges, st);
+    else if (KB == 2)
+        ok = launch_bilinear<2>(pred_cb, succ_cb, cand_ids, unary, hp, 1, anchor, Ti, S, k, (int)V, R, edges, st);
+    else
+        ok = launch_bilinear<4>(pred_cb, succ_cb, cand_ids, unary, hp, 1, anchor, Ti, S, k, (int)V, R, edges, st);
+    if (!ok) return DFLASH_ERR_UNSUPPORTED;
+    DFLASH_LAUNCH_CHECK();
+    return DFLASH_OK;
+}

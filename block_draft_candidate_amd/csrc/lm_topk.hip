@@ -116,7 +116,7 @@ template <int BN, int KCAP, bool TAIL>
 __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ W, int T, int V, int Hd,
     int nM, int nN, int G, int xmx, float s, float c, float inv_c,
-    uint64_t* __restrict__ part) {
+    uint64_t* __restrict__ part, const uint16_t* __restrict__ Wp, int R, float* __restrict__ hp) {
     constexpr int WN = BN / 2;               // columns per wave
     constexpr int NB = WN / 32;              // 32-column MFMA blocks per wave
     constexpr int MB = 4;                    // 32-row MFMA blocks per wave (128 rows)
@@ -173,10 +173,34 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const int a_row0 = (wm * 128 + fr) * LM_BK;
     const int b_row0 = (wn * WN + fr) * LM_BK;
 
-    for (int nt = n_begin; nt < n_end; ++nt) {
-        const int n0 = nt * BN;
+    // The rank projection, when hp is given: W_proj's R rows are appended to the
+    // vocabulary's columns, and the epilogue stores the staged raw fp32 sums of
+    // those columns to hp instead of selecting from them.
+    //  - merged: the last vocabulary tile has room for them (V % BN > 0 is a
+    //    multiple of a wave's BN / 4 DMA rows, R <= BN - V % BN, R % 4 == 0);
+    //    there the waves past the vocabulary rows load W_proj's rows instead, so
+    //    the projection costs no MFMA work (those columns were zeros anyway);
+    //  - else group 0 (which has the fewest tiles) runs ceil(R / BN) extra
+    //    tiles of W_proj after its own.  (Run first, they would put group 0 a
+    //    tile behind the groups that share its H slices in L2 for the whole
+    //    kernel: +17% fetched bytes.)
+    const int vtail = V % BN;
+    const bool merged = hp != nullptr && vtail > 0 && vtail % (BN / 4) == 0 && R <= BN - vtail && R % 4 == 0;
+    const int nproj = (hp != nullptr && !merged && g == 0) ? (R + BN - 1) / BN : 0;
+    for (int nt = n_begin; nt < n_end + nproj; ++nt) {
+        const bool proj = nt >= n_end;
+        const bool mixed = merged && nt == nN - 1;
+        const int n0 = (proj ? nt - n_end : nt) * BN;
+        // B operand of this wave: vocabulary rows, or (projection tiles, and the
+        // waves past the vocabulary rows of the mixed tile) W_proj's rows, with
+        // the rsrc based so that tile row vtail + i is W_proj row i
+        const bool wproj = proj || (mixed && wave_s * (BN / 4) >= vtail);
+        const uint64_t bbase = proj ? (uint64_t)(uintptr_t)(Wp + (int64_t)n0 * Hd)
+                               : mixed && wproj ? (uint64_t)(uintptr_t)Wp - (uint64_t)vtail * (uint64_t)Hd * 2u
+                                                : (uint64_t)(uintptr_t)(W + (int64_t)n0 * Hd);
+        const int brows = proj ? min(BN, R - n0) : mixed && wproj ? vtail + R : min(BN, V - n0);
         const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(W + (int64_t)n0 * Hd), (short)0, min(BN, V - n0) * Hd * 2, 0x00020000);
+            (void*)(uintptr_t)bbase, (short)0, brows * Hd * 2, 0x00020000);
         // LDS-DMA lane offsets, recomputed per tile (from opaque copies of Hd
         // and the lane, so that they are not hoisted): kept live across the
         // epilogue they get spilled, and each reload waits for every load in
@@ -282,6 +306,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
         __builtin_amdgcn_s_barrier();
         compiler_fence();
 
+
         // Epilogue, two passes: the columns of wave wn = pass are staged
         // row-major with a row pitch of QCOLS + 4 floats (the 32-lane halves of
         // a 4-byte write cover 32 consecutive columns of one row; 16-byte reads
@@ -317,7 +342,25 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging writes done
             __builtin_amdgcn_s_barrier();
             compiler_fence();
-            if (my_row < T) {
+            if (my_row < T && proj) {
+                // a projection tile: the row's raw fp32 sums (no scale, cap or
+                // selection) go to hp; columns past R were read as zero
+                const int cbase = n0 + pass * QCOLS;
+                const int ncols = min(QCOLS, R - cbase);
+                const float* rowp = stage + tid * SP;
+                // (the address from an opaque copy of the row: hoisted out of the
+                // tile loop it would be spilled, and its reload waits for every
+                // load in flight)
+                int row_t = my_row;
+                asm volatile("" : "+v"(row_t));
+                float* dstp = hp + (int64_t)row_t * R + cbase;
+                if ((R & 3) == 0) {
+                    for (int cc = 0; cc < ncols; cc += 4)
+                        *reinterpret_cast<f32x4*>(dstp + cc) = *reinterpret_cast<const f32x4*>(rowp + cc);
+                } else {
+                    for (int cc = 0; cc < ncols; ++cc) dstp[cc] = rowp[cc];
+                }
+            } else if (my_row < T) {
                 const int cbase = n0 + pass * QCOLS;
                 const int ncols = min(QCOLS, V - cbase);
                 const float* rowp = stage + tid * SP;
@@ -392,6 +435,18 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                     v = vn;
                 }
                 if (changed && list[KCAP - 1] != 0u) thr = acc_lower_bound(list[KCAP - 1] >> 16, s, c);
+            }
+            if (my_row < T && mixed) {
+                // the mixed tile's projection columns V .. V + R - 1 (R % 4 == 0,
+                // V % 4 == 0: 16-byte aligned)
+                const int cbase = n0 + pass * QCOLS;
+                const int c0 = max(0, V - cbase), c1 = min(QCOLS, V + R - cbase);
+                const float* rowp = stage + tid * SP;
+                int row_t = my_row;
+                asm volatile("" : "+v"(row_t));
+                float* dstp = hp + (int64_t)row_t * R + (cbase - V);
+                for (int cc = c0; cc < c1; cc += 4)
+                    *reinterpret_cast<f32x4*>(dstp + cc) = *reinterpret_cast<const f32x4*>(rowp + cc);
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): row reads done before the next pass writes
             __builtin_amdgcn_s_barrier();
@@ -553,25 +608,34 @@ static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p) {
     return true;
 }
 
+// The rank projection rides along when Wp / hp are given (R rows of Wp, hp
+// [T, R] fp32); else Wp = hp = NULL, R = 0.
+struct LmProj {
+    const uint16_t* Wp;
+    int R;
+    float* hp;
+};
+
 template <int BN, int KCAP>
 static void launch_tiles(const LmPlan& p, const uint16_t* H, const uint16_t* W, int T, int V, int Hd,
-                         float s, float c, uint64_t* part, hipStream_t st) {
+                         float s, float c, uint64_t* part, const LmProj& pj, hipStream_t st) {
     const float inv_c = c > 0.f ? 1.0f / c : 0.f;
     if (Hd % LM_BK == 0)
         hipLaunchKernelGGL((lm_topk_tiles<BN, KCAP, false>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H, W,
-                           T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part);
+                           T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
     else
         hipLaunchKernelGGL((lm_topk_tiles<BN, KCAP, true>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H, W,
-                           T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part);
+                           T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
 }
 
 template <int KCAP>
 static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, int T, int V, int Hd, int k,
-                       float s, float c, uint64_t* part, int32_t* ids, float* logits, hipStream_t st) {
+                       float s, float c, uint64_t* part, int32_t* ids, float* logits, const LmProj& pj,
+                       hipStream_t st) {
     if (p.BN == 256)
-        launch_tiles<256, KCAP>(p, H, W, T, V, Hd, s, c, part, st);
+        launch_tiles<256, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
     else
-        launch_tiles<128, KCAP>(p, H, W, T, V, Hd, s, c, part, st);
+        launch_tiles<128, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
     if (p.G <= 16)
         hipLaunchKernelGGL((lm_topk_merge16<KCAP>), dim3((T + 15) / 16), dim3(256), 0, st, part, T, p.G, k, ids,
                            logits);
@@ -590,9 +654,9 @@ extern "C" size_t dflash_lm_topk_workspace_size(int64_t T, int64_t V, int64_t Hd
     return p.ws;
 }
 
-extern "C" int dflash_lm_topk(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd,
-                              int32_t k, float output_multiplier, float softcap, int32_t* ids,
-                              float* logits, void* ws, size_t ws_bytes, void* stream) {
+static int lm_topk_common(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd, int32_t k,
+                          float output_multiplier, float softcap, int32_t* ids, float* logits, void* ws,
+                          size_t ws_bytes, const LmProj& pj, void* stream) {
     if (!H || !W || !ids || !logits || !ws) return DFLASH_ERR_INVALID_ARG;
     if (!DFLASH_ALIGNED16(H) || !DFLASH_ALIGNED16(W) || !DFLASH_ALIGNED16(ws)) return DFLASH_ERR_INVALID_ARG;
     if (T < 1 || V < 1 || Hd < 1 || k < 1 || k > V) return DFLASH_ERR_INVALID_ARG;
@@ -608,12 +672,30 @@ extern "C" int dflash_lm_topk(const uint16_t* H, const uint16_t* W, int64_t T, i
     uint64_t* part = reinterpret_cast<uint64_t*>(ws);
     const int Ti = (int)T, Vi = (int)V, Hi = (int)Hd;
     switch (p.KCAP) {
-        case 4: launch_all<4>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, st); break;
-        case 8: launch_all<8>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, st); break;
-        case 16: launch_all<16>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, st); break;
-        case 32: launch_all<32>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, st); break;
-        default: launch_all<64>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, st); break;
+        case 4: launch_all<4>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, pj, st); break;
+        case 8: launch_all<8>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, pj, st); break;
+        case 16: launch_all<16>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, pj, st); break;
+        case 32: launch_all<32>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, pj, st); break;
+        default: launch_all<64>(p, H, W, Ti, Vi, Hi, k, output_multiplier, c, part, ids, logits, pj, st); break;
     }
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
+}
+
+extern "C" int dflash_lm_topk(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd,
+                              int32_t k, float output_multiplier, float softcap, int32_t* ids,
+                              float* logits, void* ws, size_t ws_bytes, void* stream) {
+    return lm_topk_common(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, ws, ws_bytes,
+                          LmProj{nullptr, 0, nullptr}, stream);
+}
+
+extern "C" int dflash_lm_topk_proj(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd,
+                                   int32_t k, float output_multiplier, float softcap, const uint16_t* W_proj,
+                                   int32_t R, int32_t* ids, float* logits, float* hp, void* ws, size_t ws_bytes,
+                                   void* stream) {
+    if (!W_proj || !hp || !DFLASH_ALIGNED16(W_proj) || !DFLASH_ALIGNED16(hp)) return DFLASH_ERR_INVALID_ARG;
+    if (R < 1) return DFLASH_ERR_INVALID_ARG;
+    if (R > 4096 || (int64_t)R * Hd * 2 > INT32_MAX || T * (int64_t)R * 4 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    return lm_topk_common(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, ws, ws_bytes,
+                          LmProj{W_proj, R, hp}, stream);
 }

@@ -9,6 +9,9 @@
  *                               soft cap = final_logit_softcapping);
  *   - dflash_candidate_edges    DFlash2BeamCandidateSelector (class docstring and
  *                               forward: edge scores [requests, steps, top_k, top_k]);
+ *   - dflash_lm_topk_proj       dflash_lm_topk plus the selector's hidden_projection
+ *                               in the same pass over the hidden states, and
+ *     dflash_candidate_edges_hp the edge scores from that projection;
  *   - dflash_qk_norm_rope_cache DFlash2BeamAttention.forward, the fused per-head
  *                               q/k RMSNorm + NeoX RoPE + slot-mapped cache write;
  *   - dflash_block_attn         DFlash2BeamAttention: non-causal sliding-window
@@ -112,6 +115,45 @@ int dflash_candidate_edges(const uint16_t* pred_cb, const uint16_t* succ_cb,
                            const int32_t* anchor,
                            int64_t Rq, int32_t S, int32_t k, int64_t V, int32_t R, int64_t Hd,
                            float* edges, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The LM-head top-k of dflash_lm_topk with the selector's rank projection
+ * computed in the same pass over H (the projection is the separate
+ * hidden_projection linear layer of DFlash2BeamCandidateSelector; here
+ * W_proj's rows are appended to the LM head's column tiles, so H is read once
+ * for both):
+ *
+ *   ids, logits       exactly as dflash_lm_topk returns them (bit-identical)
+ *   hp[t, i]          = sum_j W_proj[i, j] * H[t, j]   fp32 [T, R], not rounded
+ *                       (MFMA accumulation order; no scale, cap or selection)
+ *
+ *   W_proj            bf16 [R, Hd]
+ *   ws                dflash_lm_topk_workspace_size(T, V, Hd, k) bytes
+ *
+ * Requirements: those of dflash_lm_topk; 1 <= R <= 4096; W_proj and hp 16-byte
+ * aligned.  Deterministic.
+ * ---------------------------------------------------------------------- */
+int dflash_lm_topk_proj(const uint16_t* H, const uint16_t* W,
+                        int64_t T, int64_t V, int64_t Hd, int32_t k,
+                        float output_multiplier, float softcap,
+                        const uint16_t* W_proj, int32_t R,
+                        int32_t* ids, float* logits, float* hp,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Candidate-selector edge scores from a given projection hp (fp32 [Rq*S, R],
+ * e.g. from dflash_lm_topk_proj): the formula of dflash_candidate_edges with
+ * hp[r*S + p, i] in place of the projection.  No workspace.
+ *
+ * Requirements: Rq, S, V >= 1; 1 <= k <= min(V, 64); R % 16 == 0, 16 <= R <= 256.
+ * Ids and anchors outside [0, V) are clamped into range.  Deterministic;
+ * edges[r, 0, q, :] is bit-identical for every q.
+ * ---------------------------------------------------------------------- */
+int dflash_candidate_edges_hp(const uint16_t* pred_cb, const uint16_t* succ_cb,
+                              const int32_t* cand_ids, const float* unary, const float* hp,
+                              const int32_t* anchor,
+                              int64_t Rq, int32_t S, int32_t k, int64_t V, int32_t R,
+                              float* edges, void* stream);
 
 /* ------------------------------------------------------------------------
  * RoPE table for dflash_qk_norm_rope_cache (get_rope with NeoX pairing,

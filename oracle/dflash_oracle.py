@@ -131,20 +131,26 @@ def lm_topk(H, W, k: int, multiplier: float = 1.0, softcap: float = 0.0, rows=No
 # --------------------------------------------------------------------------
 # Candidate-selector edge scores
 # --------------------------------------------------------------------------
-def candidate_edges(P, S, ids, U, H, Wp, anchor) -> np.ndarray:
-    """Edge scores ``E[r, p, q, c]`` (fp32, ``[requests, steps, k, k]``).
+def rank_projection(H, Wp) -> np.ndarray:
+    """``hidden_projection``: h_p = Wp . h, the bias-free hidden -> rank linear
+    layer of the selector, in float64.  ``H`` bf16 ``[T, hidden]``, ``Wp`` bf16
+    ``[rank, hidden]``; returns ``[T, rank]``."""
+    return bf16_to_f64(H) @ bf16_to_f64(Wp).T
 
-    h_p = Wp . h_{r,p}  (the bias-free hidden -> rank projection, float64);
+
+def candidate_edges_from_hp(P, S, ids, U, hp, anchor) -> np.ndarray:
+    """Edge scores ``E[r, p, q, c]`` (fp32, ``[requests, steps, k, k]``) from the
+    projected hidden states ``hp`` (``[Rq*steps, rank]``, row ``r*steps + p``):
+
     pred(r, 0, q) = anchor[r] for every q, pred(r, p, q) = ids[r, p-1, q];
     E[r,p,q,c] = U[r,p,c] + sum_i P[pred,i] * h_p[i] * S[ids[r,p,c], i].
 
     ``P``, ``S``: bf16 ``[vocab, rank]``; ``ids`` int ``[Rq, steps, k]``;
-    ``U`` fp32 ``[Rq, steps, k]``; ``H`` bf16 ``[Rq*steps, hidden]`` (row
-    ``r*steps + p``); ``Wp`` bf16 ``[rank, hidden]``; ``anchor`` int ``[Rq]``.
+    ``U`` fp32 ``[Rq, steps, k]``; ``anchor`` int ``[Rq]``.
     """
     Rq, St, k = ids.shape
     R = P.shape[1]
-    hp = (bf16_to_f64(H) @ bf16_to_f64(Wp).T).reshape(Rq, St, R)
+    hp = np.asarray(hp, dtype=np.float64).reshape(Rq, St, R)
     pred = np.empty_like(ids)
     pred[:, 0, :] = np.asarray(anchor)[:, None]
     pred[:, 1:, :] = ids[:, :-1, :]
@@ -155,6 +161,13 @@ def candidate_edges(P, S, ids, U, H, Wp, anchor) -> np.ndarray:
     bil = np.einsum("rpqi,rpci->rpqc", a, b)
     E = np.asarray(U, dtype=np.float64)[:, :, None, :] + bil
     return E.astype(np.float32)
+
+
+def candidate_edges(P, S, ids, U, H, Wp, anchor) -> np.ndarray:
+    """Edge scores of the selector from the hidden states ``H`` (bf16
+    ``[Rq*steps, hidden]``) and the projection ``Wp`` (bf16 ``[rank, hidden]``):
+    ``candidate_edges_from_hp`` of ``rank_projection(H, Wp)``."""
+    return candidate_edges_from_hp(P, S, ids, U, rank_projection(H, Wp), anchor)
 
 
 # --------------------------------------------------------------------------

@@ -132,3 +132,32 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(B.DFlashError):
         B.lib()
+
+
+def test_lm_topk_proj_host_validation(L):
+    f = L.dflash_lm_topk_proj
+    ws = L.dflash_lm_topk_workspace_size(8, 1024, 256, 4)
+
+    def call(Wp=FAKE, R=16, hp=FAKE, wsb=ws, k=4):
+        return f(FAKE, FAKE, 8, 1024, 256, k, 1.0, 0.0, Wp, R, FAKE, FAKE, hp, FAKE, wsb, None)
+
+    assert call(Wp=None) == 1
+    assert call(hp=None) == 1
+    assert call(hp=FAKE + 4) == 1    # misaligned
+    assert call(R=0) == 1
+    assert call(R=5000) == 2
+    assert call(k=0) == 1            # the LM-head checks still apply
+    assert call(wsb=ws - 1) == 3
+
+
+def test_edges_hp_host_validation(L):
+    f = L.dflash_candidate_edges_hp
+
+    def call(hp=FAKE, k=4, V=1024, R=16):
+        return f(FAKE, FAKE, FAKE, FAKE, hp, FAKE, 2, 4, k, V, R, FAKE, None)
+
+    assert call(hp=None) == 1
+    assert call(k=0) == 1
+    assert call(R=24) == 2          # R % 16
+    assert call(R=512) == 2         # R > 256
+    assert call(k=65, V=4096) == 2

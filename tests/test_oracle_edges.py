@@ -149,3 +149,50 @@ def test_brute_force_loops_tiny_workload():
                     acc = float(d["U"][r, p, c])
                     bil = sum(Pf[pred, i] * hp[i] * Sf[cid, i] for i in range(R))
                     assert E[r, p, q, c] == pytest.approx(acc + bil, rel=1e-6, abs=1e-7)
+
+
+def test_rank_projection_selects_hidden_columns():
+    # W_proj rows that are unit vectors pick columns of H exactly (a closed form
+    # that a transposed operand or a dropped term would break)
+    rng = np.random.default_rng(5)
+    T, Hd, R = 6, 40, 8
+    H = WL.to_bf16_bits(rng.standard_normal((T, Hd)).astype(np.float32))
+    cols = rng.choice(Hd, R, replace=False)
+    Wp = np.zeros((R, Hd), dtype=np.float32)
+    Wp[np.arange(R), cols] = 1.0
+    Wp[3, cols[5]] = 2.0                      # one row sums two columns
+    hp = O.rank_projection(H, WL.to_bf16_bits(Wp))
+    Hf = O.bf16_to_f64(H)
+    want = Hf[:, cols].copy()
+    want[:, 3] += 2.0 * Hf[:, cols[5]]
+    assert hp.shape == (T, R)
+    assert np.array_equal(hp, want)
+
+
+def test_rank_projection_brute_force():
+    d = _case(Rq=1, St=3, Hd=24, R=5, seed=11)
+    hp = O.rank_projection(d["H"], d["Wp"])
+    Hf, Wf = O.bf16_to_f64(d["H"]), O.bf16_to_f64(d["Wp"])
+    for t in range(3):
+        for i in range(5):
+            assert hp[t, i] == pytest.approx(sum(Wf[i, j] * Hf[t, j] for j in range(24)), rel=1e-12)
+
+
+def test_edges_from_hp_matches_edges_and_brute_force():
+    d = _case(Rq=2, St=3, k=3, V=40, Hd=16, R=8, seed=12)
+    hp = O.rank_projection(d["H"], d["Wp"])
+    E = O.candidate_edges_from_hp(d["P"], d["S"], d["ids"], d["U"], hp, d["anchor"])
+    assert np.array_equal(E, _E(d))
+    # a given hp that no H could give: the brute-force bilinear form on it
+    rng = np.random.default_rng(13)
+    hq = rng.standard_normal(hp.shape)
+    E2 = O.candidate_edges_from_hp(d["P"], d["S"], d["ids"], d["U"], hq, d["anchor"]).astype(np.float64)
+    Pf, Sf = O.bf16_to_f64(d["P"]), O.bf16_to_f64(d["S"])
+    for r in range(2):
+        for p in range(3):
+            for q in range(3):
+                pred = d["anchor"][r] if p == 0 else d["ids"][r, p - 1, q]
+                for c in range(3):
+                    want = float(d["U"][r, p, c]) + sum(Pf[pred, i] * hq[r * 3 + p, i] * Sf[d["ids"][r, p, c], i]
+                                                        for i in range(8))
+                    assert E2[r, p, q, c] == pytest.approx(want, rel=1e-6, abs=1e-7)
