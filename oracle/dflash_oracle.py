@@ -27,6 +27,11 @@ speculator ``vllm.v1.worker.gpu.spec_decode.dflash.speculator``):
   -> ``candidate_edges``;
 * ``DFlash2BeamAttention.forward`` (per-head q/k RMSNorm, NeoX RoPE, slot-mapped
   K/V cache write) -> ``qk_norm_rope_cache``;
+* ``DFlash2BeamModel.build_context_kv_weights`` and
+  ``precompute_and_store_context_kv`` (``hidden_norm`` RMSNorm of the context
+  states, one bf16 linear against every layer's stacked K/V rows, then every
+  layer's K-norm + RoPE and K/V cache write) -> ``rms_norm``, ``context_kv``,
+  ``store_context_kv``;
 * ``DFlash2BeamAttention.__init__`` (every layer non-causal sliding-window
   attention, scale ``head_dim ** -0.5``, GQA) and the speculator's query block of
   one anchor plus N mask tokens per request -> ``block_attn``.
@@ -41,6 +46,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "f64_to_bf16", "f64_to_f32", "lm_logit_keys", "lm_topk",
     "candidate_edges", "qk_norm_rope_cache", "block_attn", "attention_window",
+    "rank_projection", "candidate_edges_from_hp", "rms_norm", "context_kv", "store_context_kv",
 ]
 
 
@@ -229,6 +235,57 @@ def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float,
             cache_out[b, :, o, :D] = k_out[t]
             cache_out[b, :, o, D:] = v_bits[t]
     return q_out, k_out, cache_out
+
+
+# --------------------------------------------------------------------------
+# Context K/V precompute: hidden_norm, the stacked K/V linear, store_context_kv
+# --------------------------------------------------------------------------
+def rms_norm(x, w, eps: float) -> np.ndarray:
+    """``ops.rms_norm``: y = x * (mean(x^2) + eps)^-1/2 * w over the last axis,
+    in float64 with one bf16 rounding at the output (the reading taken for every
+    norm here: the pages show only the call).  ``x`` bf16 ``[..., d]``, ``w``
+    bf16 ``[d]``; returns bf16 bits."""
+    return f64_to_bf16(_rms_norm(bf16_to_f64(x), bf16_to_f64(w), eps))
+
+
+def context_kv(context_states, hidden_norm_w, eps: float, W_ctx, L: int, Hkv: int, D: int) -> np.ndarray:
+    """``precompute_and_store_context_kv`` up to the store: the ``hidden_norm``
+    RMSNorm of the context states, then ``F.linear`` with the stacked K/V rows of
+    every layer's ``qkv_proj`` (``W_ctx`` bf16 ``[L * 2 * Hkv * D, hidden]``, layer
+    l's K rows then its V rows), the product summed in float64 and rounded once
+    to the bf16 output.  Returns bf16 bits ``[num_ctx, L, 2, Hkv, D]``."""
+    normed = rms_norm(context_states, hidden_norm_w, eps)
+    kv = bf16_to_f64(normed) @ bf16_to_f64(W_ctx).T
+    return f64_to_bf16(kv).reshape(np.asarray(context_states).shape[0], L, 2, Hkv, D)
+
+
+def store_context_kv(kv, k_norm_w, eps: float, positions, theta: float, slots, caches, block_size: int = 16):
+    """``store_context_kv``: for every layer l at once, K = the layer's K-norm
+    (weights ``k_norm_w[l]``) and NeoX RoPE at the context token's position (the
+    keys the drafter's queries attend to carry both, like its own keys), one
+    bf16 rounding; V unchanged.  Token t with ``slots[t] >= 0`` writes them to
+    ``caches[l][slot // bs, h, slot % bs, :D]`` and ``[..., D:]``; negative slots
+    write nothing.
+
+    ``kv`` bf16 ``[num_ctx, L, 2, Hkv, D]``; ``k_norm_w`` bf16 ``[L, D]``;
+    ``caches`` a list of L bf16 arrays ``[blocks, Hkv, bs, 2D]``.  Returns the
+    list of updated caches.
+    """
+    kv = np.asarray(kv)
+    n, L, _, Hkv, D = kv.shape
+    ang = rope_angles(positions, D, theta)[:, None, :]  # [n, 1, D/2]
+    out = [np.array(c, copy=True) for c in caches]
+    for l in range(L):
+        k = _neox_rotate(_rms_norm(bf16_to_f64(kv[:, l, 0]), bf16_to_f64(k_norm_w[l]), eps), ang)
+        k_bits = f64_to_bf16(k)
+        for t in range(n):
+            s = int(slots[t])
+            if s < 0:
+                continue
+            b, o = divmod(s, block_size)
+            out[l][b, :, o, :D] = k_bits[t]
+            out[l][b, :, o, D:] = kv[t, l, 1]
+    return out
 
 
 # --------------------------------------------------------------------------
