@@ -15,7 +15,7 @@ import torch
 __all__ = [
     "DFlashError", "lib", "lm_topk", "lm_topk_workspace_size", "lm_topk_proj", "candidate_edges",
     "candidate_edges_workspace_size", "candidate_edges_hp", "rope_cos_sin", "qk_norm_rope_cache", "block_attn",
-    "LIB_PATH",
+    "context_kv", "context_kv_workspace_size", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
@@ -41,6 +41,10 @@ _SIGS = {
                                                  _c_f32, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32,
                                                  _c_p, _c_p, _c_p]),
     "dflash_block_attn_workspace_size": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
+    "dflash_context_kv_workspace_size": (_c_sz, [_c_i64, _c_i64]),
+    "dflash_context_kv": (ctypes.c_int, [_c_p, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                         _c_p, _c_f32, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32,
+                                         _c_p, _c_p, _c_sz, _c_p]),
     "dflash_block_attn": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i64, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_sz, _c_p]),
 }
@@ -262,3 +266,49 @@ def block_attn(q, kv_cache, block_tables, seq_lens, Lq: int, window: int, scale:
         _dev(out, torch.bfloat16, "out"), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "dflash_block_attn")
     return out
+
+
+# ---------------------------------------------------------------- context K/V precompute
+def context_kv_workspace_size(num_ctx: int, Hd: int) -> int:
+    return int(lib().dflash_context_kv_workspace_size(num_ctx, Hd))
+
+
+def context_kv(ctx_states, hidden_norm_w, hidden_eps: float, W_kv, L: int, Hkv: int, D: int, k_norm_w,
+               k_eps: float, positions, cos_sin, slots=None, caches=None, kv_out=None, want_kv: bool = False,
+               workspace=None, stream=None):
+    """Context K/V of every draft layer: ``hidden_norm`` of ``ctx_states
+    [num_ctx, Hd]`` (bf16), the stacked K/V linear ``W_kv [L*2*Hkv*D, Hd]``,
+    then each layer's K-norm (``k_norm_w [L, D]``) + NeoX RoPE and the write of
+    K and V into ``caches[l]`` (``[num_blocks, Hkv, bs, 2D]`` bf16) at ``slots``.
+    Returns ``kv_out`` (``[num_ctx, L, 2, Hkv, D]``, the linear's output before
+    the K norm) when ``want_kv`` or ``kv_out`` is given, else None."""
+    n, Hd = ctx_states.shape
+    if W_kv.shape != (L * 2 * Hkv * D, Hd) or k_norm_w.shape != (L, D) or hidden_norm_w.shape != (Hd,):
+        raise ValueError("shape mismatch between context states, hidden_norm, W_kv and k_norm_w")
+    if (slots is None) != (caches is None):
+        raise ValueError("slots and caches go together")
+    dev = ctx_states.device
+    if want_kv and kv_out is None:
+        kv_out = torch.empty((n, L, 2, Hkv, D), dtype=torch.bfloat16, device=dev)
+    ptrs, nblk, bs = None, 0, 0
+    if caches is not None:
+        if len(caches) != L:
+            raise ValueError("one cache per layer")
+        c0 = caches[0]
+        nblk, bs = c0.shape[0], c0.shape[2]
+        for c in caches:
+            if c.shape != (nblk, Hkv, bs, 2 * D):
+                raise ValueError("every cache must be [num_blocks, Hkv, block_size, 2D]")
+        ptrs = (ctypes.c_void_p * L)(*[_dev(c, torch.bfloat16, "cache") for c in caches])
+    ws = _workspace(context_kv_workspace_size(n, Hd), dev, workspace)
+    st = lib().dflash_context_kv(
+        _dev(ctx_states, torch.bfloat16, "ctx_states"), _dev(hidden_norm_w, torch.bfloat16, "hidden_norm_w"),
+        float(hidden_eps), _dev(W_kv, torch.bfloat16, "W_kv"), n, Hd, L, Hkv, D,
+        _dev(k_norm_w, torch.bfloat16, "k_norm_w"), float(k_eps), _dev(positions, torch.int64, "positions"),
+        _dev(cos_sin, torch.float32, "cos_sin"), cos_sin.shape[0],
+        None if slots is None else _dev(slots, torch.int64, "slots"),
+        None if ptrs is None else ctypes.cast(ptrs, ctypes.c_void_p), nblk, bs,
+        None if kv_out is None else _dev(kv_out, torch.bfloat16, "kv_out"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dflash_context_kv")
+    return kv_out

@@ -16,7 +16,10 @@
  *                               q/k RMSNorm + NeoX RoPE + slot-mapped cache write;
  *   - dflash_block_attn         DFlash2BeamAttention: non-causal sliding-window
  *                               attention of the query block over the cache
- *                               (scale head_dim ** -0.5, grouped K/V heads).
+ *                               (scale head_dim ** -0.5, grouped K/V heads);
+ *   - dflash_context_kv         DFlash2BeamModel.precompute_and_store_context_kv:
+ *                               hidden_norm, the stacked K/V linear of every
+ *                               draft layer, K-norm + RoPE and the cache writes.
  *
  * Conventions for every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller; bf16 tensors
@@ -199,6 +202,48 @@ int dflash_qk_norm_rope_cache(const uint16_t* qkv, int64_t row_stride,
                               const int64_t* slots, uint16_t* kv_cache,
                               int64_t num_blocks, int32_t block_size,
                               uint16_t* q_out, uint16_t* k_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Context K/V precompute for every draft layer at once
+ * (DFlash2BeamModel.build_context_kv_weights, precompute_and_store_context_kv
+ * and the store_context_kv op it calls):
+ *   normed = bf16(x * (mean(x^2) + hidden_eps)^-1/2 * hidden_norm_w)   per row of ctx_states
+ *   kv     = bf16(normed @ W_kv^T)  viewed as [num_ctx, L, 2, Hkv, D]  (fp32 accumulate)
+ * then for layer l, kv head h and token t with a cache row:
+ *   K = kv[t, l, 0, h, :] through the layer's K RMSNorm (weight k_norm_w[l], k_eps)
+ *       and the NeoX rotation of dflash_qk_norm_rope_cache at positions[t]
+ *       (fp32 inside, one bf16 rounding);
+ *   caches[l][slot / block_size, h, slot % block_size, 0:D]  = K
+ *   caches[l][slot / block_size, h, slot % block_size, D:2D] = kv[t, l, 1, h, :]
+ * Negative slots (padding) and slots >= num_blocks * block_size write nothing.
+ *
+ *   ctx_states     bf16 [num_ctx, Hd]
+ *   hidden_norm_w  bf16 [Hd]
+ *   W_kv           bf16 [L * 2 * Hkv * D, Hd]: layer l's K rows (Hkv * D), then
+ *                  its V rows, for l = 0 .. L-1 (each layer's qkv_proj rows past q)
+ *   k_norm_w       bf16 [L, D]
+ *   positions      int64 [num_ctx]  (clamped into [0, max_pos))
+ *   cos_sin        fp32 [max_pos, D]  (dflash_rope_cos_sin)
+ *   slots          int64 [num_ctx] or NULL
+ *   caches         HOST array of L DEVICE pointers, each bf16
+ *                  [num_blocks, Hkv, block_size, 2D] (one layer's cache), or NULL.
+ *                  slots and caches are both NULL (no cache write: the linear
+ *                  alone, as for a profiling run) or both non-NULL; the array
+ *                  itself is read during the call only.
+ *   kv_out         bf16 [num_ctx, L, 2, Hkv, D] or NULL: kv before the K norm
+ *   ws             dflash_context_kv_workspace_size(num_ctx, Hd) bytes
+ *                  (the normed states)
+ * Requirements: D == 128; Hd % 8 == 0; 1 <= L <= 64; num_ctx, Hkv >= 1.
+ * ---------------------------------------------------------------------- */
+size_t dflash_context_kv_workspace_size(int64_t num_ctx, int64_t Hd);
+int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hidden_norm_w, float hidden_eps,
+                      const uint16_t* W_kv, int64_t num_ctx, int64_t Hd,
+                      int32_t L, int32_t Hkv, int32_t D,
+                      const uint16_t* k_norm_w, float k_eps,
+                      const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                      const int64_t* slots, uint16_t* const* caches,
+                      int64_t num_blocks, int32_t block_size,
+                      uint16_t* kv_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Non-causal sliding-window block attention over a paged cache

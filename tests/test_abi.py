@@ -161,3 +161,30 @@ def test_edges_hp_host_validation(L):
     assert call(R=24) == 2          # R % 16
     assert call(R=512) == 2         # R > 256
     assert call(k=65, V=4096) == 2
+
+
+def test_context_kv_host_validation(L):
+    f = L.dflash_context_kv
+    n, Hd, Lyr, Hkv, D = 300, 320, 2, 2, 128
+    ws = L.dflash_context_kv_workspace_size(n, Hd)
+    assert ws == n * Hd * 2
+    assert L.dflash_context_kv_workspace_size(0, Hd) == 0
+    caches = (ctypes.c_void_p * 64)(*([FAKE] * 64))
+    bad = (ctypes.c_void_p * 2)(FAKE, FAKE + 8)
+
+    def call(ctx=FAKE, slots=FAKE, cp=caches, Lyr=Lyr, D=D, Hd=Hd, wsb=ws, eps=1e-6, kvo=None, nblk=64):
+        return f(ctx, FAKE, eps, FAKE, n, Hd, Lyr, Hkv, D, FAKE, 1e-6, FAKE, FAKE, 4096, slots,
+                 ctypes.cast(cp, ctypes.c_void_p) if cp is not None else None, nblk, 16, kvo, FAKE, wsb, None)
+
+    assert call(ctx=None) == 1
+    assert call(ctx=FAKE + 2) == 1        # misaligned
+    assert call(slots=None) == 1          # exactly one of slots / caches
+    assert call(cp=None) == 1
+    assert call(cp=bad) == 1              # a misaligned layer cache
+    assert call(nblk=0) == 1
+    assert call(eps=-1.0) == 1
+    assert call(kvo=FAKE + 4) == 1
+    assert call(D=64) == 2
+    assert call(Hd=324) == 2              # Hd % 8
+    assert call(Lyr=65) == 2
+    assert call(wsb=ws - 1) == 3

@@ -43,3 +43,18 @@ def test_attention_layout():
     # slots of the query block point into the request's own blocks
     r = np.repeat(np.arange(4), d["query_len"])
     assert np.all(d["slots"] // bs == d["block_tables"][r, d["positions"] // bs])
+
+
+def test_context_kv_inputs_layout():
+    d = WL.context_kv_inputs("ctx_small", pad_fraction=0.1)
+    n, bs = d["num_ctx"], d["block_size"]
+    s = d["slots"]
+    live = s[s >= 0]
+    assert len(set(live.tolist())) == live.size                    # one token per slot
+    assert live.max() < d["num_blocks"] * bs
+    assert np.array_equal(live % bs, d["positions"][s >= 0] % bs)  # offset in block = position % bs
+    assert (s < 0).any()
+    assert d["W_kv"].shape == (d["layers"] * 2 * d["hkv"] * d["head_dim"], d["hidden"])
+    assert d["k_norm_w"].shape == (d["layers"], d["head_dim"])
+    assert d["hidden"] % 64 != 0                                   # the K-tail case
+    assert n % 256 != 0 and n > 256                                # a ragged second row tile

@@ -55,6 +55,21 @@ CONFIGS = {
     ),
 }
 
+# Context K/V precompute (every draft layer's K/V of the context tokens from one
+# stacked linear): the attention workload's shapes (128 requests, 16 new
+# context tokens each, 8 kv heads of 128, eps 1e-6, theta 1e6, 16-token
+# blocks) with the drafter's hidden size of the full candidate head.
+CONTEXT_CONFIGS = {
+    # sized for the CPU oracle: two row tiles (one ragged), four column tiles,
+    # hidden 328 (not a multiple of 64: the K-tail path)
+    "ctx_small": dict(requests=20, tokens=15, hidden=328, layers=2, hkv=2, head_dim=128,
+                      ctx_lo=0, ctx_hi=3000, block_size=16, eps=1e-6, theta=1e6, seed=106),
+    "ctx": dict(requests=128, tokens=16, hidden=4096,
+                layers=5,  # chosen: the pages do not give the drafter's layer count
+                hkv=8, head_dim=128, ctx_lo=512, ctx_hi=8192, block_size=16, eps=1e-6, theta=1e6,
+                seed=107),
+}
+
 SIGMA_W = 0.02  # N(0, 0.02) init of the LM head, codebooks and projection
 
 _CHUNK = 1 << 22  # elements per independent random stream (fixed: results do not
@@ -258,4 +273,50 @@ def qk_inputs(name: str = "mid", pad_fraction: float = 0.0) -> dict:
     return dict(qkv=qkv, q_w=q_w, k_w=k_w, positions=positions, slots=slots,
                 cache=cache, tokens=Tq, hq=Hq, hkv=Hkv, head_dim=D, block_size=bs,
                 num_blocks=nblk, eps=qc["eps"], theta=qc["theta"],
+                max_pos=int(positions.max()) + 1)
+
+
+def context_kv_inputs(name: str = "ctx", pad_fraction: float = 0.0) -> dict:
+    """Inputs of the context K/V precompute for workload ``name``.
+
+    Request r has ``ctx_r`` tokens cached (uniform in ``[ctx_lo, ctx_hi]``) and
+    adds ``tokens`` context tokens at positions ``ctx_r .. ctx_r + tokens - 1``;
+    each token's slot comes from the request's block table (physical blocks a
+    random permutation).  Context states N(0,1), W_kv N(0, 0.02), the
+    hidden_norm and K-norm weights 1 + 0.1 N(0,1), all bf16.  The layer caches
+    are not drawn here (a caller fills them).  ``pad_fraction`` of the slots
+    are set to -1, the skip value.
+    """
+    c = CONTEXT_CONFIGS[name]
+    seed = c["seed"]
+    Rq, Lt, Hd, L, Hkv, D, bs = (c["requests"], c["tokens"], c["hidden"], c["layers"], c["hkv"],
+                                 c["head_dim"], c["block_size"])
+    n = Rq * Lt
+    ctx_states = bf16_normal(seed, 0, (n, Hd))
+    hn_w = to_bf16_bits(normal_f32(seed, 1, Hd, 0.1) + np.float32(1.0))
+    W_kv = bf16_normal(seed, 2, (L * 2 * Hkv * D, Hd), SIGMA_W)
+    k_norm_w = to_bf16_bits(normal_f32(seed, 3, L * D, 0.1) + np.float32(1.0)).reshape(L, D)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 4])))
+    ctx = g.integers(c["ctx_lo"], c["ctx_hi"] + 1, size=Rq, dtype=np.int64)
+    positions = (ctx[:, None] + np.arange(Lt)[None, :]).reshape(-1).astype(np.int64)
+    # blocks holding the new tokens only: the rest of each request's table is
+    # irrelevant to this step
+    first = ctx // bs
+    last = (ctx + Lt - 1) // bs
+    nblk = int((last - first + 1).sum())
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 5])))
+    perm = g.permutation(nblk).astype(np.int64)
+    slots = np.empty(n, dtype=np.int64)
+    off = 0
+    for r in range(Rq):
+        nb = int(last[r] - first[r] + 1)
+        p = positions[r * Lt:(r + 1) * Lt]
+        slots[r * Lt:(r + 1) * Lt] = perm[off + (p // bs - first[r])] * bs + p % bs
+        off += nb
+    if pad_fraction > 0:
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 6])))
+        slots[g.random(n) < pad_fraction] = -1
+    return dict(ctx_states=ctx_states, hidden_norm_w=hn_w, W_kv=W_kv, k_norm_w=k_norm_w,
+                positions=positions, slots=slots, num_ctx=n, hidden=Hd, layers=L, hkv=Hkv,
+                head_dim=D, block_size=bs, num_blocks=nblk, eps=c["eps"], theta=c["theta"],
                 max_pos=int(positions.max()) + 1)
