@@ -13,6 +13,10 @@ One step = the whole hot path over one synthetic batch, inputs resident in HBM:
 With --two-kernel-edges, steps 1-2 are dflash_lm_topk and dflash_candidate_edges
 (projection and edges in their own two kernels).
 
+Also timed, on its own and outside the step: dflash_context_kv, the context
+K/V precompute of 2048 context tokens for 5 draft layers (reported under
+kernels.context_kv).
+
 Prints one JSON line.  `value` is edge scores per second of the whole step.
 Per-kernel times come from HIP events on the stream the kernels run on; the
 roofline object is for the dominant kernel (the LM-head top-k, MFMA-bound).
@@ -93,6 +97,15 @@ def attn_work(seq_lens, Lq, Hq, Hkv, D, window):
         vis += int((L - lo).sum())
     flops = 4 * D * Hq * vis
     return nbytes, flops
+
+
+def context_kv_work(n, Hd, L, Hkv, D):
+    """Algorithmic bytes (context states, hidden_norm and K-norm weights, W_kv,
+    positions, slots, the tokens' RoPE rows, K and V written to every layer's
+    cache) and flops of the stacked linear."""
+    N = L * 2 * Hkv * D
+    nbytes = n * Hd * 2 + Hd * 2 + N * Hd * 2 + L * D * 2 + n * 8 * 2 + n * D * 4 + n * N * 2
+    return nbytes, 2 * n * N * Hd
 
 
 def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, key):
@@ -199,6 +212,8 @@ def main():
     ap.add_argument("--two-kernel-edges", action="store_true",
                     help="LM head and edges as dflash_lm_topk + dflash_candidate_edges (projection in the edge "
                          "call) instead of dflash_lm_topk_proj + dflash_candidate_edges_hp")
+    ap.add_argument("--no-context-kv", action="store_true",
+                    help="skip the separately timed context K/V precompute (dflash_context_kv)")
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="the oracle baseline runs 1/N of the step's requests (default 4: about 10-20 s on 16 cores)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -319,6 +334,46 @@ def main():
     edges_per_step = Rq * S * k * k
     value = edges_per_step / (ms_per_step / 1e3)
 
+    # the context K/V precompute that precedes a draft step (every draft
+    # layer's K/V of the step's new context tokens), timed on its own: it is
+    # not part of the step above
+    ctx_kernel = None
+    if not args.no_context_kv:
+        log("context K/V precompute ...")
+        cx = WL.context_kv_inputs("ctx")
+        n_c, Hd_c, L_c, Hkv_c, D_c = cx["num_ctx"], cx["hidden"], cx["layers"], cx["hkv"], cx["head_dim"]
+        c_states, c_hw, c_W, c_kw = dbf(cx["ctx_states"]), dbf(cx["hidden_norm_w"]), dbf(cx["W_kv"]), dbf(cx["k_norm_w"])
+        c_pos = torch.from_numpy(cx["positions"]).to(dev)
+        c_slots = torch.from_numpy(cx["slots"]).to(dev)
+        c_cs = B.rope_cos_sin(cx["max_pos"], D_c, cx["theta"], dev)
+        c_caches = [torch.zeros((cx["num_blocks"], Hkv_c, cx["block_size"], 2 * D_c), dtype=torch.bfloat16,
+                                device=dev) for _ in range(L_c)]
+        c_ws = torch.empty(B.context_kv_workspace_size(n_c, Hd_c), dtype=torch.uint8, device=dev)
+
+        def ctx_call():
+            B.context_kv(c_states, c_hw, cx["eps"], c_W, L_c, Hkv_c, D_c, c_kw, cx["eps"], c_pos, c_cs, c_slots,
+                         c_caches, workspace=c_ws)
+        for _ in range(args.warmup):
+            ctx_call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c_ms = 0.0
+        for _ in range(args.steps):
+            e0.record()
+            ctx_call()
+            e1.record()
+            torch.cuda.synchronize()
+            c_ms += e0.elapsed_time(e1)
+        c_ms /= args.steps
+        cb, cf = context_kv_work(n_c, Hd_c, L_c, Hkv_c, D_c)
+        ctx_kernel = {"ms": c_ms, "TFLOP_per_s": cf / (c_ms * 1e-3) / 1e12,
+                      "mfma_frac": cf / (c_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                      "GB_per_s": cb / (c_ms * 1e-3) / 1e9, "hbm_frac": cb / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "algorithmic_bytes": cb, "flops": cf,
+                      "workload": f"{n_c} context tokens (128 requests x 16), hidden {Hd_c}, {L_c} draft layers x "
+                                  f"{Hkv_c} kv heads x head_dim {D_c}; hidden_norm + stacked K/V linear + K-norm/RoPE "
+                                  "+ cache writes (not part of the step)"}
+
     Rp = R if fused else 0
     lmb, lmf = lm_bytes(T, V, Hd, k, Rp), lm_flops(T, V, Hd, Rp)
     eb = edge_bytes(Rq, S, k, R, Hd, from_hp=fused)
@@ -379,6 +434,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if ctx_kernel is not None:
+        result["kernels"]["context_kv"] = ctx_kernel
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(cand, attn, edges_per_step, args.cpu_sample)

@@ -9,12 +9,12 @@
 //     is reduced across the workgroup, the normed row is written once as bf16
 //     (the norm's output dtype) into the workspace.
 //   * ctx_kv_tiles: the stacked linear as a bf16 MFMA GEMM (32x32x16, fp32
-//     accumulate) over 256 x 256 output tiles, with the same operand pipeline as
-//     the LM head's tile kernel (64-wide K slices by LDS-DMA into a five-slot LDS
-//     ring, XOR-swizzled 16-byte chunks).  A tile's 256 columns are two whole
-//     heads (head_dim 128) of one layer's K or V, so each wave-column half holds
-//     one head for 128 rows and the epilogue needs no data from other tiles:
-//     the half is staged row-major in LDS, thread t takes row t, rounds the fp32
+//     accumulate) over 256 x 256 or 256 x 128 output tiles, with the same
+//     operand pipeline as the LM head's tile kernel (64-wide K slices by LDS-DMA
+//     into a five-slot LDS ring, XOR-swizzled 16-byte chunks).  A tile's columns
+//     are whole heads (head_dim 128) of one layer's K or V, so the epilogue
+//     needs no data from other tiles: a head's columns are staged row-major in
+//     LDS, thread t takes row t, rounds the fp32
 //     sums to bf16 (the linear's output), and for a K head applies the layer's
 //     RMSNorm over the 128 values and the NeoX rotation at the token's position
 //     before one more bf16 rounding; V is stored as rounded.  The row then goes
@@ -28,7 +28,6 @@
 namespace dflash {
 
 constexpr int CKV_BM = 256;
-constexpr int CKV_BN = 256;
 constexpr int CKV_BK = 64;
 constexpr int CKV_THREADS = 256;
 constexpr int CKV_D = 128;
@@ -85,24 +84,24 @@ __global__ __launch_bounds__(256) void ctx_hidden_norm_kernel(const uint16_t* __
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
 
-template <bool TAIL>
+template <int BN, bool TAIL>
 __global__ __launch_bounds__(CKV_THREADS, 1) void ctx_kv_tiles(
     const uint16_t* __restrict__ A /*normed [n, Hd]*/, const uint16_t* __restrict__ W /*[N, Hd]*/, int n, int Hd,
     int N, int nM, int ntiles, int Hkv, const uint16_t* __restrict__ k_w /*[L, D]*/, float eps,
     const int64_t* __restrict__ positions, const float* __restrict__ cos_sin, int64_t max_pos,
     const int64_t* __restrict__ slots, CtxCaches caches, int64_t num_blocks, int block_size,
     uint16_t* __restrict__ kv_out) {
-    constexpr int BN = CKV_BN;
-    constexpr int WN = BN / 2;               // columns per wave = one head
+    constexpr int WN = BN / 2;               // columns per wave
     constexpr int NB = WN / 32;              // 32-column MFMA blocks per wave
     constexpr int MB = 4;                    // 32-row MFMA blocks per wave (128 rows)
     constexpr int NIA = CKV_BM / 8 / 4;      // LDS-DMA instructions per wave per slice (A)
     constexpr int NIB = BN / 8 / 4;          // (B)
     constexpr int UNIT = CKV_BM * CKV_BK;    // elements of one operand's K slice
     constexpr int NSLOT = 5;                 // LDS ring of operand slices (2.5 K slices)
-    constexpr int SP = WN + 4;               // row pitch (floats) of the epilogue staging
+    constexpr int SP = CKV_D + 4;            // row pitch (floats) of the epilogue staging (one head)
     constexpr int SMEM = (NSLOT * UNIT > CKV_BM * SP * 2) ? NSLOT * UNIT : CKV_BM * SP * 2;
-    static_assert(WN == CKV_D, "a wave-column half is one head");
+    constexpr int NPASS = BN / CKV_D;        // heads per tile = epilogue passes
+    static_assert(BN % CKV_D == 0 && (WN % CKV_D == 0 || CKV_D % WN == 0), "heads align with wave columns");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
     float* stage = reinterpret_cast<float*>(smem);
 
@@ -235,15 +234,16 @@ __global__ __launch_bounds__(CKV_THREADS, 1) void ctx_kv_tiles(
     }
     const int64_t head_stride = (int64_t)block_size * 2 * CKV_D;
 
-    // Two passes, one per head (wave-column half): stage the half row-major
-    // (pitch WN + 4 floats), then thread t finishes row t.  In the 32x32 MFMA
-    // layout lane l holds column l % 32 and rows 8b + 4(l / 32) + e, e = 0..3.
+    // One pass per head of the tile: the waves holding the head's columns
+    // stage them row-major (pitch D + 4 floats), then thread t finishes row t.
+    // In the 32x32 MFMA layout lane l holds column l % 32 and rows
+    // 8b + 4(l / 32) + e, e = 0..3.
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        if (wn == pass) {
+    for (int pass = 0; pass < NPASS; ++pass) {
+        if ((wn * WN) / CKV_D == pass) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const int col = j * 32 + fr;
+                const int col = (wn * WN) % CKV_D + j * 32 + fr;
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(CKV_THREADS, 1) void ctx_kv_tiles(
         compiler_fence();
         if (my_row < n) {
             // head (layer l, K or V, kv head h) of these 128 columns
-            const int gh = (n0 >> 7) + pass;
+            const int gh = n0 / CKV_D + pass;
             const int l = gh / (2 * Hkv);
             const int r = gh - l * 2 * Hkv;
             const bool is_v = r >= Hkv;
@@ -386,10 +386,20 @@ extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hid
     if (D != CKV_D || Hd % 8 != 0 || L > CKV_MAX_LAYERS) return DFLASH_ERR_UNSUPPORTED;
     const int64_t N = (int64_t)L * 2 * Hkv * D;
     if (num_ctx > INT32_MAX || N > INT32_MAX || Hd > (int64_t)1 << 20) return DFLASH_ERR_UNSUPPORTED;
-    if ((int64_t)CKV_BN * Hd * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    if ((int64_t)256 * Hd * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     if (ws_bytes < dflash_context_kv_workspace_size(num_ctx, Hd)) return DFLASH_ERR_WORKSPACE;
+    // Tile width: 256 columns (two heads) or 128 (one head), whichever needs
+    // fewer tile-rounds of the device's compute units, weighting a round by
+    // the tile's width (one 256 x BN tile per CU at a time).
     const int nM = (int)((num_ctx + CKV_BM - 1) / CKV_BM);
-    const int64_t ntiles = (int64_t)nM * (N / CKV_BN);
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
+    }
+    auto cost = [&](int64_t bn) { return ((nM * (N / bn) + ncu - 1) / ncu) * bn; };
+    const int BN = cost(128) < cost(256) ? 128 : 256;
+    const int64_t ntiles = (int64_t)nM * (N / BN);
     if (ntiles > (int64_t)1 << 28) return DFLASH_ERR_UNSUPPORTED;
     const int per = (int)((ntiles + 7) / 8);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -397,14 +407,19 @@ extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hid
     hipLaunchKernelGGL(ctx_hidden_norm_kernel, dim3((unsigned)num_ctx), dim3(256), 0, st, ctx_states, hidden_norm_w,
                        (int)Hd, hidden_eps, normed);
     const dim3 grid((unsigned)(8 * per));
-    if (Hd % CKV_BK == 0)
-        hipLaunchKernelGGL(ctx_kv_tiles<false>, grid, dim3(CKV_THREADS), 0, st, normed, W_kv, (int)num_ctx, (int)Hd,
-                           (int)N, nM, (int)ntiles, (int)Hkv, k_norm_w, k_eps, positions, cos_sin, max_pos, slots,
-                           cp, num_blocks, (int)block_size, kv_out);
-    else
-        hipLaunchKernelGGL(ctx_kv_tiles<true>, grid, dim3(CKV_THREADS), 0, st, normed, W_kv, (int)num_ctx, (int)Hd,
-                           (int)N, nM, (int)ntiles, (int)Hkv, k_norm_w, k_eps, positions, cos_sin, max_pos, slots,
-                           cp, num_blocks, (int)block_size, kv_out);
+#define CKV_LAUNCH(BNV, TL)                                                                                         \
+    hipLaunchKernelGGL((ctx_kv_tiles<BNV, TL>), grid, dim3(CKV_THREADS), 0, st, normed, W_kv, (int)num_ctx, (int)Hd, \
+                       (int)N, nM, (int)ntiles, (int)Hkv, k_norm_w, k_eps, positions, cos_sin, max_pos, slots, cp,    \
+                       num_blocks, (int)block_size, kv_out)
+    const bool tail = Hd % CKV_BK != 0;
+    if (BN == 256) {
+        if (tail) CKV_LAUNCH(256, true);
+        else CKV_LAUNCH(256, false);
+    } else {
+        if (tail) CKV_LAUNCH(128, true);
+        else CKV_LAUNCH(128, false);
+    }
+#undef CKV_LAUNCH
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
 }

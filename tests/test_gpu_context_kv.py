@@ -109,6 +109,11 @@ def test_context_kv_single_token_one_layer(B):
     _check(B, d, "n=1,L=1")
 
 
+def test_context_kv_wide_tiles(B):
+    # 4096 tokens x 8192 columns: the 256-column tile variant (with the K tail)
+    _check(B, WL.context_kv_inputs("ctx_wide", pad_fraction=0.05), "wide")
+
+
 def test_context_kv_full_workload(B):
     # 128 requests x 16 context tokens, hidden 4096, 5 layers of 8 kv heads
     d = WL.context_kv_inputs("ctx")

@@ -64,6 +64,10 @@ CONTEXT_CONFIGS = {
     # hidden 328 (not a multiple of 64: the K-tail path)
     "ctx_small": dict(requests=20, tokens=15, hidden=328, layers=2, hkv=2, head_dim=128,
                       ctx_lo=0, ctx_hi=3000, block_size=16, eps=1e-6, theta=1e6, seed=106),
+    # many tiles over a short K (hidden 136, a K tail): 16 row tiles x 8192
+    # columns, where 256-column tiles need no more rounds than 128-column ones
+    "ctx_wide": dict(requests=256, tokens=16, hidden=136, layers=4, hkv=8, head_dim=128,
+                     ctx_lo=0, ctx_hi=9000, block_size=16, eps=1e-6, theta=1e6, seed=108),
     "ctx": dict(requests=128, tokens=16, hidden=4096,
                 layers=5,  # chosen: the pages do not give the drafter's layer count
                 hkv=8, head_dim=128, ctx_lo=512, ctx_hi=8192, block_size=16, eps=1e-6, theta=1e6,
