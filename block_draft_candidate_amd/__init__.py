@@ -15,7 +15,7 @@ import torch
 __all__ = [
     "DFlashError", "lib", "lm_topk", "lm_topk_workspace_size", "lm_topk_proj", "candidate_edges",
     "candidate_edges_workspace_size", "candidate_edges_hp", "rope_cos_sin", "qk_norm_rope_cache", "block_attn",
-    "context_kv", "context_kv_workspace_size", "LIB_PATH",
+    "context_kv", "context_kv_workspace_size", "linear", "draft_attention", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
@@ -42,6 +42,7 @@ _SIGS = {
                                                  _c_p, _c_p, _c_p]),
     "dflash_block_attn_workspace_size": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
     "dflash_context_kv_workspace_size": (_c_sz, [_c_i64, _c_i64]),
+    "dflash_linear": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p]),
     "dflash_context_kv": (ctypes.c_int, [_c_p, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                          _c_p, _c_f32, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32,
                                          _c_p, _c_p, _c_sz, _c_p]),
@@ -312,3 +313,33 @@ def context_kv(ctx_states, hidden_norm_w, hidden_eps: float, W_kv, L: int, Hkv: 
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "dflash_context_kv")
     return kv_out
+
+
+# ---------------------------------------------------------------- draft-layer projections
+def linear(X, W, out=None, stream=None) -> torch.Tensor:
+    """``bf16(X [M, K] . W [N, K]^T)`` (bias-free nn.Linear, fp32 accumulate)."""
+    if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1]:
+        raise ValueError("X must be [M, K] and W [N, K]")
+    M, K = X.shape
+    N = W.shape[0]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device) if out is None else out
+    if out.dim() != 2 or out.shape[0] != M or out.shape[1] < N or out.stride(1) != 1 or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16 [M, >= N] with unit column stride")
+    st = lib().dflash_linear(_dev(X, torch.bfloat16, "X"), _dev(W, torch.bfloat16, "W"), M, N, K, out.data_ptr(),
+                             out.stride(0), _stream(stream))
+    _check(st, "dflash_linear")
+    return out
+
+
+def draft_attention(hidden, W_qkv, W_o, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, positions, cos_sin,
+                    slots, kv_cache, block_tables, seq_lens, Lq: int, window: int, stream=None) -> torch.Tensor:
+    """One draft attention sublayer (DFlash2BeamAttention.forward) on the
+    query block: ``qkv_proj``, the fused q/k norm + RoPE + cache write, the
+    non-causal window attention over the cache, ``o_proj``.  Four calls into the
+    library; returns ``[T, hidden]`` bf16."""
+    T = hidden.shape[0]
+    qkv = linear(hidden, W_qkv, stream=stream)
+    q, _ = qk_norm_rope_cache(qkv, Hq, Hkv, D, q_w, k_w, eps, positions, cos_sin, slots, kv_cache,
+                              want_k=False, stream=stream)
+    o = block_attn(q, kv_cache, block_tables, seq_lens, Lq, window, stream=stream)
+    return linear(o.view(T, Hq * D), W_o, stream=stream)

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdflash.so")
-SOURCES = ["lm_topk.hip", "edges.hip", "qk_norm_rope.hip", "block_attn.hip", "context_kv.hip", "api.hip"]
+SOURCES = ["lm_topk.hip", "edges.hip", "qk_norm_rope.hip", "block_attn.hip", "context_kv.hip", "linear.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

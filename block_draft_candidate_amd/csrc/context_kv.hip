@@ -23,13 +23,10 @@
 //     unless the caller asks for it.
 //   * Tiles are dealt to XCDs in contiguous runs (row tiles fastest), so the
 //     workgroups of an XCD share weight tiles and context slices in its L2.
-#include "common.h"
+#include "gemm_tile.h"
 
 namespace dflash {
 
-constexpr int CKV_BM = 256;
-constexpr int CKV_BK = 64;
-constexpr int CKV_THREADS = 256;
 constexpr int CKV_D = 128;
 constexpr int CKV_MAX_LAYERS = 64;
 
@@ -38,10 +35,6 @@ constexpr int CKV_MAX_LAYERS = 64;
 struct CtxCaches {
     uint16_t* p[CKV_MAX_LAYERS];
 };
-
-__device__ __forceinline__ uint32_t ckv_lds_offset(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // ---------------------------------------------------------------------------
 // hidden_norm: normed[t, :] = bf16(x[t, :] * (mean(x[t, :]^2) + eps)^-1/2 * w)
@@ -85,139 +78,31 @@ __global__ __launch_bounds__(256) void ctx_hidden_norm_kernel(const uint16_t* __
 __device__ __forceinline__ float bf16_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
 
 template <int BN, bool TAIL>
-__global__ __launch_bounds__(CKV_THREADS, 1) void ctx_kv_tiles(
+__global__ __launch_bounds__(GT_THREADS, 1) void ctx_kv_tiles(
     const uint16_t* __restrict__ A /*normed [n, Hd]*/, const uint16_t* __restrict__ W /*[N, Hd]*/, int n, int Hd,
     int N, int nM, int ntiles, int Hkv, const uint16_t* __restrict__ k_w /*[L, D]*/, float eps,
     const int64_t* __restrict__ positions, const float* __restrict__ cos_sin, int64_t max_pos,
     const int64_t* __restrict__ slots, CtxCaches caches, int64_t num_blocks, int block_size,
     uint16_t* __restrict__ kv_out) {
-    constexpr int WN = BN / 2;               // columns per wave
-    constexpr int NB = WN / 32;              // 32-column MFMA blocks per wave
-    constexpr int MB = 4;                    // 32-row MFMA blocks per wave (128 rows)
-    constexpr int NIA = CKV_BM / 8 / 4;      // LDS-DMA instructions per wave per slice (A)
-    constexpr int NIB = BN / 8 / 4;          // (B)
-    constexpr int UNIT = CKV_BM * CKV_BK;    // elements of one operand's K slice
-    constexpr int NSLOT = 5;                 // LDS ring of operand slices (2.5 K slices)
-    constexpr int SP = CKV_D + 4;            // row pitch (floats) of the epilogue staging (one head)
-    constexpr int SMEM = (NSLOT * UNIT > CKV_BM * SP * 2) ? NSLOT * UNIT : CKV_BM * SP * 2;
+    constexpr int SP = GT_SP;                // row pitch (floats) of the epilogue staging (one head)
     constexpr int NPASS = BN / CKV_D;        // heads per tile = epilogue passes
-    static_assert(BN % CKV_D == 0 && (WN % CKV_D == 0 || CKV_D % WN == 0), "heads align with wave columns");
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
+    static_assert(BN % CKV_D == 0, "tiles hold whole heads");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[GT_SMEM];
     float* stage = reinterpret_cast<float*>(smem);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // Workgroup ids go to the 8 XCDs round-robin; XCD x takes tiles
-    // [x * per, (x + 1) * per) in (column tile, row tile) order.
-    const int per = gridDim.x >> 3;
-    const int q = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (q >= ntiles) return;
-    const int m_tile = q % nM, n_tile = q / nM;
-    const int m0 = m_tile * CKV_BM;
+    int m_tile, n_tile;
+    if (!gemm_tile_index(ntiles, nM, m_tile, n_tile)) return;
+    const int m0 = m_tile * GT_BM;
     const int n0 = n_tile * BN;
     const int my_row = m0 + tid;
 
-    const int nK = (Hd + CKV_BK - 1) / CKV_BK;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A + (int64_t)m0 * Hd), (short)0, min(CKV_BM, n - m0) * Hd * 2, 0x00020000);
+        (void*)(A + (int64_t)m0 * Hd), (short)0, min(GT_BM, n - m0) * Hd * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(W + (int64_t)n0 * Hd), (short)0, BN * Hd * 2, 0x00020000);
-
-    const int fr = lane & 31;
-    const int a_row0 = (wm * 128 + fr) * CKV_BK;
-    const int b_row0 = (wn * WN + fr) * CKV_BK;
-    int voffA[NIA], voffB[NIB], lcA, lcB;
-    dma_offsets<NIA>(voffA, lcA, wave_s, lane, Hd);
-    dma_offsets<NIB>(voffB, lcB, wave_s, lane, Hd);
-
-    f32x16 acc[MB][NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    // Fragment qf of one 16-wide K step (A0, B0..B{NB-1}, A1..A{MB-1}: the order
-    // the MFMAs consume them) of the slice whose halves sit in slots sa / sb.
-    constexpr int NFR = MB + NB;
-    auto read_frag = [&](int sa, int sb, int k16, int qf, bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
-        const int chs = ((2 * k16 + (lane >> 5)) ^ swz8(fr)) << 3;
-        if (qf >= 1 && qf <= NB)
-            fb[qf - 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(smem + sb * UNIT + b_row0 + (qf - 1) * 32 * CKV_BK + chs));
-        else {
-            const int i = qf == 0 ? 0 : qf - NB;
-            fa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(smem + sa * UNIT + a_row0 + i * 32 * CKV_BK + chs));
-        }
-    };
-    auto mfmas = [&](const bf16x8 (&fa)[MB], const bf16x8 (&fb)[NB]) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    };
-    // One K step: its MFMAs, with the next step's fragment reads and (dma = 1 /
-    // 2) the LDS-DMA loads of an A / B half interleaved by group barriers.
-    constexpr int MPK = MB * NB;
-    auto kstep = [&](const bf16x8 (&fa)[MB], const bf16x8 (&fb)[NB], int ra, int rb, int rk16,
-                     bf16x8 (&na)[MB], bf16x8 (&nb)[NB], int dma, int dkt, int dslot) {
-#pragma unroll
-        for (int qq = 0; qq < (NFR > NIA ? NFR : NIA); ++qq) {
-            if (qq < NFR && rk16 >= 0) read_frag(ra, rb, rk16, qq, na, nb);
-            if (dma == 1 && qq < NIA)
-                dma_one<NIA, TAIL>(rsA, smem + dslot * UNIT, voffA, lcA, wave_s, Hd, dkt * CKV_BK, qq);
-            if (dma == 2 && qq < NIB)
-                dma_one<NIB, TAIL>(rsB, smem + dslot * UNIT, voffB, lcB, wave_s, Hd, dkt * CKV_BK, qq);
-        }
-        mfmas(fa, fb);
-#pragma unroll
-        for (int qq = 0; qq < MPK; ++qq) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (qq < NFR && rk16 >= 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if ((dma == 1 && qq < NIA) || (dma == 2 && qq < NIB)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-    };
-
-    // Slice k keeps its B half in ring slot 2k mod 5 and its A half in 2k+1 mod
-    // 5; the barrier at the end of slice k frees both, the A half of slice k+2
-    // goes into one right after it and the B half of slice k+3 into the other
-    // during the first K step of slice k+1 (B in flight for about two slices).
-    bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
-    dma_slice<NIB, TAIL>(rsB, smem + 0 * UNIT, voffB, lcB, wave_s, Hd, 0);
-    dma_slice<NIA, TAIL>(rsA, smem + 1 * UNIT, voffA, lcA, wave_s, Hd, 0);
-    dma_slice<NIB, TAIL>(rsB, smem + 2 * UNIT, voffB, lcB, wave_s, Hd, CKV_BK);  // past K: zeros, unused
-    dma_slice<NIA, TAIL>(rsA, smem + 3 * UNIT, voffA, lcA, wave_s, Hd, CKV_BK);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NIB + NIA));  // slice 0 landed
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    int sb = 0, sa = 1;
-#pragma unroll
-    for (int qq = 0; qq < NFR; ++qq) read_frag(sa, sb, 0, qq, fa0, fb0);
-    for (int kt = 0; kt + 1 < nK; ++kt) {
-        const int sn = sb == 0 ? NSLOT - 1 : sb - 1;  // slot of the B half of slice kt+2
-        kstep(fa0, fb0, sa, sb, 1, fa1, fb1, 2, kt + 2, sn);
-        kstep(fa1, fb1, sa, sb, 2, fa0, fb0, 0, 0, 0);
-        kstep(fa0, fb0, sa, sb, 3, fa1, fb1, 0, 0, 0);
-        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(NIB));  // slice kt+1 landed
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
-        const int sa2 = sb;
-        sb = sb + 2 >= NSLOT ? sb + 2 - NSLOT : sb + 2;
-        sa = sa + 2 >= NSLOT ? sa + 2 - NSLOT : sa + 2;
-        kstep(fa1, fb1, sa, sb, 0, fa0, fb0, 1, kt + 2, sa2);
-    }
-    kstep(fa0, fb0, sa, sb, 1, fa1, fb1, 0, 0, 0);
-    kstep(fa1, fb1, sa, sb, 2, fa0, fb0, 0, 0, 0);
-    kstep(fa0, fb0, sa, sb, 3, fa1, fb1, 0, 0, 0);
-    kstep(fa1, fb1, sa, sb, -1, fa0, fb0, 0, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0070);
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
+    f32x16 acc[4][BN / 64];
+    gemm_tile_mainloop<BN, TAIL>(smem, rsA, rsB, Hd, acc);
 
     // Per-row data of the epilogue: the token's RoPE row and its cache row.
     int64_t pos = 0, cache_row = -1;  // element offset of [blk, 0, off, 0]
@@ -234,36 +119,11 @@ __global__ __launch_bounds__(CKV_THREADS, 1) void ctx_kv_tiles(
     }
     const int64_t head_stride = (int64_t)block_size * 2 * CKV_D;
 
-    // One pass per head of the tile: the waves holding the head's columns
-    // stage them row-major (pitch D + 4 floats), then thread t finishes row t.
-    // In the 32x32 MFMA layout lane l holds column l % 32 and rows
-    // 8b + 4(l / 32) + e, e = 0..3.
+    // One pass per head of the tile: the head's 128 columns are staged
+    // row-major, then thread t finishes row t.
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-        if ((wn * WN) / CKV_D == pass) {
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int col = (wn * WN) % CKV_D + j * 32 + fr;
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        // 4-byte writes straight from the accumulator registers
-                        const uint32_t dst =
-                            ckv_lds_offset(stage + (wm * 128 + i * 32 + 8 * b + 4 * (lane >> 5)) * SP + col);
-                        asm volatile("ds_write_b32 %0, %1" ::"v"(dst), "a"(acc[i][j][4 * b]) : "memory");
-                        asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(dst), "a"(acc[i][j][4 * b + 1]),
-                                     "i"(SP * 4) : "memory");
-                        asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(dst), "a"(acc[i][j][4 * b + 2]),
-                                     "i"(SP * 8) : "memory");
-                        asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(dst), "a"(acc[i][j][4 * b + 3]),
-                                     "i"(SP * 12) : "memory");
-                    }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging writes done
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
+        gemm_tile_stage<BN>(stage, acc, pass);
         if (my_row < n) {
             // head (layer l, K or V, kv head h) of these 128 columns
             const int gh = n0 / CKV_D + pass;
@@ -346,9 +206,7 @@ __global__ __launch_bounds__(CKV_THREADS, 1) void ctx_kv_tiles(
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): row reads done before the next pass writes
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
+        gemm_tile_pass_done();
     }
 }
 
@@ -389,16 +247,9 @@ extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hid
     if ((int64_t)256 * Hd * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     if (ws_bytes < dflash_context_kv_workspace_size(num_ctx, Hd)) return DFLASH_ERR_WORKSPACE;
     // Tile width: 256 columns (two heads) or 128 (one head), whichever needs
-    // fewer tile-rounds of the device's compute units, weighting a round by
-    // the tile's width (one 256 x BN tile per CU at a time).
-    const int nM = (int)((num_ctx + CKV_BM - 1) / CKV_BM);
-    int dev = 0, ncu = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
-    }
-    auto cost = [&](int64_t bn) { return ((nM * (N / bn) + ncu - 1) / ncu) * bn; };
-    const int BN = cost(128) < cost(256) ? 128 : 256;
+    // fewer tile-rounds of the device's compute units.
+    const int nM = (int)((num_ctx + GT_BM - 1) / GT_BM);
+    const int BN = gemm_tile_width(num_ctx, N);
     const int64_t ntiles = (int64_t)nM * (N / BN);
     if (ntiles > (int64_t)1 << 28) return DFLASH_ERR_UNSUPPORTED;
     const int per = (int)((ntiles + 7) / 8);
@@ -408,10 +259,10 @@ extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hid
                        (int)Hd, hidden_eps, normed);
     const dim3 grid((unsigned)(8 * per));
 #define CKV_LAUNCH(BNV, TL)                                                                                         \
-    hipLaunchKernelGGL((ctx_kv_tiles<BNV, TL>), grid, dim3(CKV_THREADS), 0, st, normed, W_kv, (int)num_ctx, (int)Hd, \
+    hipLaunchKernelGGL((ctx_kv_tiles<BNV, TL>), grid, dim3(GT_THREADS), 0, st, normed, W_kv, (int)num_ctx, (int)Hd, \
                        (int)N, nM, (int)ntiles, (int)Hkv, k_norm_w, k_eps, positions, cos_sin, max_pos, slots, cp,    \
                        num_blocks, (int)block_size, kv_out)
-    const bool tail = Hd % CKV_BK != 0;
+    const bool tail = Hd % GT_BK != 0;
     if (BN == 256) {
         if (tail) CKV_LAUNCH(256, true);
         else CKV_LAUNCH(256, false);

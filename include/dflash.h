@@ -19,7 +19,8 @@
  *                               (scale head_dim ** -0.5, grouped K/V heads);
  *   - dflash_context_kv         DFlash2BeamModel.precompute_and_store_context_kv:
  *                               hidden_norm, the stacked K/V linear of every
- *                               draft layer, K-norm + RoPE and the cache writes.
+ *                               draft layer, K-norm + RoPE and the cache writes;
+ *   - dflash_linear             the draft layer's bias-free qkv_proj / o_proj.
  *
  * Conventions for every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller; bf16 tensors
@@ -244,6 +245,22 @@ int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hidden_norm_w,
                       const int64_t* slots, uint16_t* const* caches,
                       int64_t num_blocks, int32_t block_size,
                       uint16_t* kv_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Bias-free linear with a bf16 output, for the draft layer's projections
+ * around its attention (DFlash2BeamAttention: qkv_proj, whose output row is
+ * the q|k|v row of dflash_qk_norm_rope_cache, and o_proj on the attention
+ * output):
+ *   Y[m, n] = bf16( sum_k X[m, k] * W[n, k] )     (fp32 accumulate, one rounding)
+ *
+ *   X  bf16 [M, K]
+ *   W  bf16 [N, K]   (nn.Linear's weight: out x in)
+ *   Y  bf16 [M, ldy], columns 0 .. N-1 written, the rest untouched
+ * Requirements: M, N, K >= 1; ldy >= N; N, K, ldy multiples of 8.
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+int dflash_linear(const uint16_t* X, const uint16_t* W, int64_t M, int64_t N, int64_t K,
+                  uint16_t* Y, int64_t ldy, void* stream);
 
 /* ------------------------------------------------------------------------
  * Non-causal sliding-window block attention over a paged cache

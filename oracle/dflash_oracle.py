@@ -32,6 +32,8 @@ speculator ``vllm.v1.worker.gpu.spec_decode.dflash.speculator``):
   states, one bf16 linear against every layer's stacked K/V rows, then every
   layer's K-norm + RoPE and K/V cache write) -> ``rms_norm``, ``context_kv``,
   ``store_context_kv``;
+* ``DFlash2BeamAttention.__init__`` / ``forward`` (bias-free ``qkv_proj`` and
+  ``o_proj`` around the attention) -> ``linear``, ``draft_attention``;
 * ``DFlash2BeamAttention.__init__`` (every layer non-causal sliding-window
   attention, scale ``head_dim ** -0.5``, GQA) and the speculator's query block of
   one anchor plus N mask tokens per request -> ``block_attn``.
@@ -47,6 +49,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "f64_to_f32", "lm_logit_keys", "lm_topk",
     "candidate_edges", "qk_norm_rope_cache", "block_attn", "attention_window",
     "rank_projection", "candidate_edges_from_hp", "rms_norm", "context_kv", "store_context_kv",
+    "linear", "draft_attention",
 ]
 
 
@@ -333,3 +336,26 @@ def block_attn(q, cache, block_tables, seq_lens, Lq: int, Hq: int, Hkv: int,
             p /= p.sum(axis=-1, keepdims=True)
             out[r, :, kh * group:(kh + 1) * group, :] = p @ Vf[:, kh, :]
     return f64_to_bf16(out.reshape(Rq * Lq, Hq, D))
+
+
+# --------------------------------------------------------------------------
+# The draft layer's projections and the whole attention sublayer
+# --------------------------------------------------------------------------
+def linear(X, W) -> np.ndarray:
+    """Bias-free ``nn.Linear`` in the model dtype: ``Y = X W^T`` summed in
+    float64, rounded once to bf16.  ``X`` bf16 ``[M, K]``, ``W`` bf16 ``[N, K]``
+    (out x in); returns bf16 bits ``[M, N]``."""
+    return f64_to_bf16(bf16_to_f64(X) @ bf16_to_f64(W).T)
+
+
+def draft_attention(hidden, W_qkv, W_o, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, positions,
+                    theta: float, slots, cache, block_tables, seq_lens, Lq: int, block_size: int, window: int):
+    """``DFlash2BeamAttention.forward`` on the query block: ``qkv_proj`` (its
+    output row is q heads, then k heads, then v heads), the fused q/k norm +
+    RoPE + cache write, the non-causal window attention of the block over the
+    cache (scale ``D ** -0.5``), ``o_proj``.  Returns ``(out bf16 [T, hidden],
+    updated cache)``."""
+    qkv = linear(hidden, W_qkv)
+    q, _, cache2 = qk_norm_rope_cache(qkv, Hq, Hkv, D, q_w, k_w, eps, positions, theta, slots, cache, block_size)
+    o = block_attn(q, cache2, block_tables, seq_lens, Lq, Hq, Hkv, D, block_size, window, D ** -0.5)
+    return linear(np.asarray(o).reshape(len(o), Hq * D), W_o), cache2

@@ -188,3 +188,18 @@ def test_context_kv_host_validation(L):
     assert call(Hd=324) == 2              # Hd % 8
     assert call(Lyr=65) == 2
     assert call(wsb=ws - 1) == 3
+
+
+def test_linear_host_validation(L):
+    f = L.dflash_linear
+
+    def call(X=FAKE, M=300, N=200, K=328, ldy=200, Y=FAKE):
+        return f(X, FAKE, M, N, K, Y, ldy, None)
+
+    assert call(X=None) == 1
+    assert call(Y=FAKE + 2) == 1
+    assert call(M=0) == 1
+    assert call(ldy=192) == 1        # ldy < N
+    assert call(N=201, ldy=208) == 2  # N % 8
+    assert call(K=330) == 2          # K % 8
+    assert call(ldy=204) == 2        # ldy % 8

@@ -324,3 +324,21 @@ def context_kv_inputs(name: str = "ctx", pad_fraction: float = 0.0) -> dict:
                 positions=positions, slots=slots, num_ctx=n, hidden=Hd, layers=L, hkv=Hkv,
                 head_dim=D, block_size=bs, num_blocks=nblk, eps=c["eps"], theta=c["theta"],
                 max_pos=int(positions.max()) + 1)
+
+
+def draft_layer_inputs(requests: int | None = None) -> dict:
+    """One draft attention sublayer on the attention workload's query block:
+    ``attention_inputs("attn", requests)`` plus the block's hidden states
+    ``[Rq*16, 4096]`` ~ N(0, 1) and the bias-free projections ``W_qkv
+    [(32 + 2*8)*128, 4096]`` and ``W_o [4096, 32*128]`` ~ N(0, 0.02), bf16."""
+    a = attention_inputs("attn", requests=requests)
+    seed = CONFIGS["attn"]["seed"]
+    hidden = 4096  # the drafter's hidden size (= the candidate head's)
+    Hq, Hkv, D = a["hq"], a["hkv"], a["head_dim"]
+    T = a["requests"] * a["query_len"]
+    a = dict(a)
+    a["hidden_states"] = bf16_normal(seed, 10, (T, hidden))
+    a["W_qkv"] = bf16_normal(seed, 11, ((Hq + 2 * Hkv) * D, hidden), SIGMA_W)
+    a["W_o"] = bf16_normal(seed, 12, (hidden, Hq * D), SIGMA_W)
+    a["hidden"] = hidden
+    return a
