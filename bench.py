@@ -15,7 +15,8 @@ With --two-kernel-edges, steps 1-2 are dflash_lm_topk and dflash_candidate_edges
 
 Also timed, on its own and outside the step: dflash_context_kv, the context
 K/V precompute of 2048 context tokens for 5 draft layers (reported under
-kernels.context_kv).
+kernels.context_kv), and dflash_linear as the draft layer's qkv_proj (2048 x
+6144 x 4096) and o_proj (2048 x 4096 x 4096) (kernels.linear_*).
 
 Prints one JSON line.  `value` is edge scores per second of the whole step.
 Per-kernel times come from HIP events on the stream the kernels run on; the
@@ -214,6 +215,8 @@ def main():
                          "call) instead of dflash_lm_topk_proj + dflash_candidate_edges_hp")
     ap.add_argument("--no-context-kv", action="store_true",
                     help="skip the separately timed context K/V precompute (dflash_context_kv)")
+    ap.add_argument("--no-draft-layer", action="store_true",
+                    help="skip the separately timed draft-layer projections (dflash_linear qkv_proj / o_proj)")
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="the oracle baseline runs 1/N of the step's requests (default 4: about 10-20 s on 16 cores)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -382,6 +385,40 @@ def main():
     lm_tflops = lmf / (kms["lm_topk"] * 1e-3) / 1e12
     lm_gbs = lmb / (kms["lm_topk"] * 1e-3) / 1e9
 
+    # the draft layer's projections around steps 3-4 (qkv_proj before the
+    # q/k norm, o_proj after the attention), timed on their own at the
+    # attention workload's 2048 query tokens; not part of the step
+    lin_kernels = {}
+    if not args.no_draft_layer:
+        log("draft-layer projections ...")
+        dl = WL.draft_layer_inputs(attn=attn)
+        x_h, w_qkv, w_o = dbf(dl["hidden_states"]), dbf(dl["W_qkv"]), dbf(dl["W_o"])
+        y_qkv = torch.empty((x_h.shape[0], w_qkv.shape[0]), dtype=torch.bfloat16, device=dev)
+        x_o = torch.empty((x_h.shape[0], w_o.shape[1]), dtype=torch.bfloat16, device=dev).normal_()
+        y_o = torch.empty((x_h.shape[0], w_o.shape[0]), dtype=torch.bfloat16, device=dev)
+        for name, (X_, W_, Y_) in (("qkv_proj", (x_h, w_qkv, y_qkv)), ("o_proj", (x_o, w_o, y_o))):
+            for _ in range(args.warmup):
+                B.linear(X_, W_, out=Y_)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            l_ms = 0.0
+            for _ in range(args.steps):
+                e0.record()
+                B.linear(X_, W_, out=Y_)
+                e1.record()
+                torch.cuda.synchronize()
+                l_ms += e0.elapsed_time(e1)
+            l_ms /= args.steps
+            Mx, Kx = X_.shape
+            Nx = W_.shape[0]
+            lf = 2 * Mx * Nx * Kx
+            lb = (Mx * Kx + Nx * Kx + Mx * Nx) * 2
+            lin_kernels["linear_" + name] = {
+                "ms": l_ms, "TFLOP_per_s": lf / (l_ms * 1e-3) / 1e12,
+                "mfma_frac": lf / (l_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "GB_per_s": lb / (l_ms * 1e-3) / 1e9, "algorithmic_bytes": lb, "flops": lf,
+                "workload": f"dflash_linear {Mx} x {Nx} x {Kx} (draft layer {name}; not part of the step)"}
+
     result = {
         "metric": METRIC,
         "value": value,
@@ -436,6 +473,7 @@ def main():
     }
     if ctx_kernel is not None:
         result["kernels"]["context_kv"] = ctx_kernel
+    result["kernels"].update(lin_kernels)
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(cand, attn, edges_per_step, args.cpu_sample)

@@ -326,12 +326,13 @@ def context_kv_inputs(name: str = "ctx", pad_fraction: float = 0.0) -> dict:
                 max_pos=int(positions.max()) + 1)
 
 
-def draft_layer_inputs(requests: int | None = None) -> dict:
+def draft_layer_inputs(requests: int | None = None, attn: dict | None = None) -> dict:
     """One draft attention sublayer on the attention workload's query block:
-    ``attention_inputs("attn", requests)`` plus the block's hidden states
-    ``[Rq*16, 4096]`` ~ N(0, 1) and the bias-free projections ``W_qkv
-    [(32 + 2*8)*128, 4096]`` and ``W_o [4096, 32*128]`` ~ N(0, 0.02), bf16."""
-    a = attention_inputs("attn", requests=requests)
+    ``attention_inputs("attn", requests)`` (or ``attn``, already drawn) plus the
+    block's hidden states ``[Rq*16, 4096]`` ~ N(0, 1) and the bias-free
+    projections ``W_qkv [(32 + 2*8)*128, 4096]`` and ``W_o [4096, 32*128]`` ~
+    N(0, 0.02), bf16."""
+    a = attention_inputs("attn", requests=requests) if attn is None else attn
     seed = CONFIGS["attn"]["seed"]
     hidden = 4096  # the drafter's hidden size (= the candidate head's)
     Hq, Hkv, D = a["hq"], a["hkv"], a["head_dim"]
