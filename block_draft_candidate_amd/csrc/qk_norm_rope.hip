@@ -16,7 +16,7 @@
 namespace dflash {
 
 constexpr int QK_D = 128;
-constexpr int QK_HPG = 4;  // heads per 16-lane group handled per round (48 heads: 3 used)
+constexpr int QK_HPG = 3;  // heads per 16-lane group handled per round (48 heads: all)
 
 __global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
     const uint16_t* __restrict__ qkv, int64_t row_stride, int Hq, int Hkv,
@@ -41,9 +41,9 @@ __global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
         }
     }
     const int64_t head_stride = (int64_t)block_size * 2 * QK_D;  // next kv head of the same block
-    float qw[8], kw[8];
-    unpack8(ldg16(q_w + j * 8), qw);
-    unpack8(ldg16(k_w + j * 8), kw);
+    // norm weights kept packed (8 bf16 in 4 registers each), widened on use
+    const u32x4 qw_raw = ldg16(q_w + j * 8);
+    const u32x4 kw_raw = ldg16(k_w + j * 8);
     const float* cs = cos_sin + pos * QK_D + (j & 7) * 8;
     const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
     const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
@@ -76,9 +76,11 @@ __global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
             for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 16);
             const float rinv = 1.0f / sqrtf(ss * (1.0f / QK_D) + eps);
             const bool is_q = h < Hq;
+            float wv[8];
+            unpack8(is_q ? qw_raw : kw_raw, wv);
             float y[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = x[e] * rinv * (is_q ? qw[e] : kw[e]);
+            for (int e = 0; e < 8; ++e) y[e] = x[e] * rinv * wv[e];
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
