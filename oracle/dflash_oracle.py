@@ -49,7 +49,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "f64_to_f32", "lm_logit_keys", "lm_topk",
     "candidate_edges", "qk_norm_rope_cache", "block_attn", "attention_window",
     "rank_projection", "candidate_edges_from_hp", "rms_norm", "context_kv", "store_context_kv",
-    "linear", "draft_attention",
+    "linear", "draft_attention", "rope_cos_sin",
 ]
 
 
@@ -204,26 +204,64 @@ def _neox_rotate(y: np.ndarray, ang: np.ndarray) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
+def rope_cos_sin(positions, rotary_dim: int, theta: float, table: str = "f64"):
+    """cos and sin of the RoPE angles ``[T, rotary_dim/2]`` (``rope_angles``
+    with the rotary dim in the exponent).  ``table="bf16"`` rounds each value
+    once to bf16, as a bf16 cos/sin cache holds them; ``"f64"`` keeps them."""
+    ang = rope_angles(positions, rotary_dim, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    if table == "bf16":
+        c, s = bf16_to_f64(f64_to_bf16(c)), bf16_to_f64(f64_to_bf16(s))
+    elif table != "f64":
+        raise ValueError(table)
+    return c, s
+
+
+def _rope(y: np.ndarray, c: np.ndarray, s: np.ndarray, neox: bool) -> np.ndarray:
+    """Rotate the first ``rotary_dim = 2 * c.shape[-1]`` elements of the last
+    axis of ``y`` by the angles whose cos / sin are ``c`` / ``s`` (broadcast
+    over the axes between): NeoX pairs ``(i, i + rotary_dim/2)``, else GPT-J
+    pairs ``(2i, 2i + 1)``, both with angle index i.  The remaining elements
+    pass unchanged."""
+    r2 = c.shape[-1]
+    out = np.array(y, dtype=np.float64, copy=True)
+    if neox:
+        x1, x2 = y[..., :r2], y[..., r2:2 * r2]
+    else:
+        x1, x2 = y[..., 0:2 * r2:2], y[..., 1:2 * r2:2]
+    o1 = x1 * c - x2 * s
+    o2 = x2 * c + x1 * s
+    if neox:
+        out[..., :r2], out[..., r2:2 * r2] = o1, o2
+    else:
+        out[..., 0:2 * r2:2], out[..., 1:2 * r2:2] = o1, o2
+    return out
+
+
 def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float,
                        positions, theta: float, slots=None, cache=None,
-                       block_size: int = 16):
+                       block_size: int = 16, rotary_dim: int | None = None,
+                       neox: bool = True, table: str = "f64"):
     """Draft layer's fused q/k norm + RoPE + cache write.
 
     ``qkv``: bf16 ``[T, (Hq + 2 Hkv) D]``, q heads, then k heads, then v heads.
     For each token and head: RMSNorm over the head (weights ``q_w``/``k_w``,
-    one eps for both), then NeoX RoPE at the token's position (rotary dim =
-    head dim), one bf16 rounding at the output.  With a cache, token t with
-    ``slots[t] >= 0`` writes K' to ``cache[slot // bs, h, slot % bs, :D]`` and
-    its V bits unchanged to ``[..., D:]``; negative slots write nothing.
+    one eps for both), then RoPE at the token's position over the first
+    ``rotary_dim`` elements (default: the head dim; NeoX pairs unless
+    ``neox=False``; cos/sin as ``rope_cos_sin(..., table)``), one bf16
+    rounding at the output.  With a cache, token t with ``slots[t] >= 0``
+    writes K' to ``cache[slot // bs, h, slot % bs, :D]`` and its V bits
+    unchanged to ``[..., D:]``; negative slots write nothing.
 
     Returns ``(q_out bf16 [T,Hq,D], k_out bf16 [T,Hkv,D], cache_out or None)``.
     """
     qkv = np.asarray(qkv)
     T = qkv.shape[0]
     x = bf16_to_f64(qkv).reshape(T, Hq + 2 * Hkv, D)
-    ang = rope_angles(positions, D, theta)[:, None, :]  # [T,1,D/2]
-    q = _neox_rotate(_rms_norm(x[:, :Hq], bf16_to_f64(q_w), eps), ang)
-    k = _neox_rotate(_rms_norm(x[:, Hq:Hq + Hkv], bf16_to_f64(k_w), eps), ang)
+    c, s = rope_cos_sin(positions, D if rotary_dim is None else rotary_dim, theta, table)
+    c, s = c[:, None, :], s[:, None, :]  # [T,1,rotary_dim/2]
+    q = _rope(_rms_norm(x[:, :Hq], bf16_to_f64(q_w), eps), c, s, neox)
+    k = _rope(_rms_norm(x[:, Hq:Hq + Hkv], bf16_to_f64(k_w), eps), c, s, neox)
     q_out = f64_to_bf16(q)
     k_out = f64_to_bf16(k)
     cache_out = None
@@ -262,7 +300,8 @@ def context_kv(context_states, hidden_norm_w, eps: float, W_ctx, L: int, Hkv: in
     return f64_to_bf16(kv).reshape(np.asarray(context_states).shape[0], L, 2, Hkv, D)
 
 
-def store_context_kv(kv, k_norm_w, eps: float, positions, theta: float, slots, caches, block_size: int = 16):
+def store_context_kv(kv, k_norm_w, eps: float, positions, theta: float, slots, caches, block_size: int = 16,
+                     rotary_dim: int | None = None, neox: bool = True, table: str = "f64"):
     """``store_context_kv``: for every layer l at once, K = the layer's K-norm
     (weights ``k_norm_w[l]``) and NeoX RoPE at the context token's position (the
     keys the drafter's queries attend to carry both, like its own keys), one
@@ -271,21 +310,23 @@ def store_context_kv(kv, k_norm_w, eps: float, positions, theta: float, slots, c
     write nothing.
 
     ``kv`` bf16 ``[num_ctx, L, 2, Hkv, D]``; ``k_norm_w`` bf16 ``[L, D]``;
-    ``caches`` a list of L bf16 arrays ``[blocks, Hkv, bs, 2D]``.  Returns the
-    list of updated caches.
+    ``caches`` a list of L bf16 arrays ``[blocks, Hkv, bs, 2D]``.  The RoPE
+    options are those of ``qk_norm_rope_cache``.  Returns the list of updated
+    caches.
     """
     kv = np.asarray(kv)
     n, L, _, Hkv, D = kv.shape
-    ang = rope_angles(positions, D, theta)[:, None, :]  # [n, 1, D/2]
-    out = [np.array(c, copy=True) for c in caches]
+    c, s = rope_cos_sin(positions, D if rotary_dim is None else rotary_dim, theta, table)
+    c, s = c[:, None, :], s[:, None, :]  # [n, 1, rotary_dim/2]
+    out = [np.array(cc, copy=True) for cc in caches]
     for l in range(L):
-        k = _neox_rotate(_rms_norm(bf16_to_f64(kv[:, l, 0]), bf16_to_f64(k_norm_w[l]), eps), ang)
+        k = _rope(_rms_norm(bf16_to_f64(kv[:, l, 0]), bf16_to_f64(k_norm_w[l]), eps), c, s, neox)
         k_bits = f64_to_bf16(k)
         for t in range(n):
-            s = int(slots[t])
-            if s < 0:
+            slot = int(slots[t])
+            if slot < 0:
                 continue
-            b, o = divmod(s, block_size)
+            b, o = divmod(slot, block_size)
             out[l][b, :, o, :D] = k_bits[t]
             out[l][b, :, o, D:] = kv[t, l, 1]
     return out
