@@ -37,6 +37,13 @@ _SIGS = {
     "dflash_candidate_edges": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32,
                                               _c_i32, _c_i64, _c_i32, _c_i64, _c_p, _c_p, _c_sz, _c_p]),
     "dflash_rope_cos_sin": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_f64, _c_p]),
+    "dflash_rope_cos_sin_bf16": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_f64, _c_p]),
+    "dflash_qk_norm_rope_cache_ex": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
+                                                    _c_f32, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
+                                                    _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+    "dflash_context_kv_ex": (ctypes.c_int, [_c_p, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                            _c_p, _c_f32, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
+                                            _c_i64, _c_i32, _c_p, _c_p, _c_sz, _c_p]),
     "dflash_qk_norm_rope_cache": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
                                                  _c_f32, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32,
                                                  _c_p, _c_p, _c_p]),
@@ -205,17 +212,32 @@ def candidate_edges_hp(pred_cb, succ_cb, cand_ids, unary, hp, anchor, out: torch
 
 
 # ---------------------------------------------------------------- q/k norm, RoPE, cache
-def rope_cos_sin(max_pos: int, D: int, theta: float, device, out=None, stream=None) -> torch.Tensor:
-    """fp32 ``[max_pos, D]`` table: cos in ``[:, :D/2]``, sin in ``[:, D/2:]``."""
-    out = torch.empty((max_pos, D), dtype=torch.float32, device=device) if out is None else out
-    _check(lib().dflash_rope_cos_sin(_dev(out, torch.float32, "cos_sin"), max_pos, D, float(theta),
-                                     _stream(stream)), "dflash_rope_cos_sin")
+def rope_cos_sin(max_pos: int, D: int, theta: float, device, out=None, stream=None,
+                 dtype=torch.float32) -> torch.Tensor:
+    """``[max_pos, D]`` table (``D`` = the rotary dim): cos in ``[:, :D/2]``,
+    sin in ``[:, D/2:]``; fp32, or bf16 with ``dtype=torch.bfloat16``."""
+    out = torch.empty((max_pos, D), dtype=dtype, device=device) if out is None else out
+    if dtype == torch.bfloat16:
+        _check(lib().dflash_rope_cos_sin_bf16(_dev(out, torch.bfloat16, "cos_sin"), max_pos, D, float(theta),
+                                              _stream(stream)), "dflash_rope_cos_sin_bf16")
+    else:
+        _check(lib().dflash_rope_cos_sin(_dev(out, torch.float32, "cos_sin"), max_pos, D, float(theta),
+                                         _stream(stream)), "dflash_rope_cos_sin")
     return out
+
+
+def _rope_args(cos_sin, D, rotary_dim, is_neox):
+    """(pointer, rotary_dim, is_neox, table_bf16) of a RoPE table argument."""
+    rot = D if rotary_dim is None else int(rotary_dim)
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != rot:
+        raise ValueError("cos_sin must be [max_pos, rotary_dim]")
+    bf = cos_sin.dtype == torch.bfloat16
+    return _dev(cos_sin, torch.bfloat16 if bf else torch.float32, "cos_sin"), rot, int(bool(is_neox)), int(bf)
 
 
 def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, positions, cos_sin,
                        slots=None, kv_cache=None, q_out=None, k_out=None, want_k: bool = True,
-                       stream=None):
+                       stream=None, rotary_dim: int | None = None, is_neox: bool = True):
     """Fused per-head RMSNorm + NeoX RoPE of the q and k heads of ``qkv``
     ``[T, >= (Hq + 2 Hkv) D]`` (bf16), writing K/V into ``kv_cache`` at
     ``slots`` when both are given.  Returns ``(q_out, k_out or None)``."""
@@ -233,15 +255,16 @@ def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, pos
         raise ValueError("kv_cache must be [num_blocks, Hkv, block_size, 2D]")
     if qkv.dtype != torch.bfloat16 or not qkv.is_cuda:
         raise TypeError("qkv must be a bf16 device tensor")
-    st = lib().dflash_qk_norm_rope_cache(
+    cs_ptr, rot, neox, tbf = _rope_args(cos_sin, D, rotary_dim, is_neox)
+    st = lib().dflash_qk_norm_rope_cache_ex(
         qkv.data_ptr(), qkv.stride(0), T, Hq, Hkv, D, _dev(q_w, torch.bfloat16, "q_w"),
         _dev(k_w, torch.bfloat16, "k_w"), float(eps), _dev(positions, torch.int64, "positions"),
-        _dev(cos_sin, torch.float32, "cos_sin"), cos_sin.shape[0],
+        cs_ptr, cos_sin.shape[0], rot, neox, tbf,
         None if slots is None else _dev(slots, torch.int64, "slots"),
         None if kv_cache is None else _dev(kv_cache, torch.bfloat16, "kv_cache"), nblk, bs,
         _dev(q_out, torch.bfloat16, "q_out"), None if k_out is None else _dev(k_out, torch.bfloat16, "k_out"),
         _stream(stream))
-    _check(st, "dflash_qk_norm_rope_cache")
+    _check(st, "dflash_qk_norm_rope_cache_ex")
     return q_out, k_out
 
 
@@ -276,7 +299,7 @@ def context_kv_workspace_size(num_ctx: int, Hd: int) -> int:
 
 def context_kv(ctx_states, hidden_norm_w, hidden_eps: float, W_kv, L: int, Hkv: int, D: int, k_norm_w,
                k_eps: float, positions, cos_sin, slots=None, caches=None, kv_out=None, want_kv: bool = False,
-               workspace=None, stream=None):
+               workspace=None, stream=None, rotary_dim: int | None = None, is_neox: bool = True):
     """Context K/V of every draft layer: ``hidden_norm`` of ``ctx_states
     [num_ctx, Hd]`` (bf16), the stacked K/V linear ``W_kv [L*2*Hkv*D, Hd]``,
     then each layer's K-norm (``k_norm_w [L, D]``) + NeoX RoPE and the write of
@@ -302,16 +325,17 @@ def context_kv(ctx_states, hidden_norm_w, hidden_eps: float, W_kv, L: int, Hkv: 
                 raise ValueError("every cache must be [num_blocks, Hkv, block_size, 2D]")
         ptrs = (ctypes.c_void_p * L)(*[_dev(c, torch.bfloat16, "cache") for c in caches])
     ws = _workspace(context_kv_workspace_size(n, Hd), dev, workspace)
-    st = lib().dflash_context_kv(
+    cs_ptr, rot, neox, tbf = _rope_args(cos_sin, D, rotary_dim, is_neox)
+    st = lib().dflash_context_kv_ex(
         _dev(ctx_states, torch.bfloat16, "ctx_states"), _dev(hidden_norm_w, torch.bfloat16, "hidden_norm_w"),
         float(hidden_eps), _dev(W_kv, torch.bfloat16, "W_kv"), n, Hd, L, Hkv, D,
         _dev(k_norm_w, torch.bfloat16, "k_norm_w"), float(k_eps), _dev(positions, torch.int64, "positions"),
-        _dev(cos_sin, torch.float32, "cos_sin"), cos_sin.shape[0],
+        cs_ptr, cos_sin.shape[0], rot, neox, tbf,
         None if slots is None else _dev(slots, torch.int64, "slots"),
         None if ptrs is None else ctypes.cast(ptrs, ctypes.c_void_p), nblk, bs,
         None if kv_out is None else _dev(kv_out, torch.bfloat16, "kv_out"),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "dflash_context_kv")
+    _check(st, "dflash_context_kv_ex")
     return kv_out
 
 

@@ -77,12 +77,36 @@ __global__ __launch_bounds__(256) void ctx_hidden_norm_kernel(const uint16_t* __
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
 
+// 8 / 4 consecutive entries of the RoPE table (fp32 or bf16) from element idx
+__device__ __forceinline__ void rope_table8(const void* t, bool bf, int64_t idx, float (&v)[8]) {
+    if (bf) {
+        unpack8(ldg16(reinterpret_cast<const uint16_t*>(t) + idx), v);
+    } else {
+        const float* f = reinterpret_cast<const float*>(t) + idx;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(f);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(f + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+    }
+}
+__device__ __forceinline__ void rope_table4(const void* t, bool bf, int64_t idx, float (&v)[4]) {
+    if (bf) {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(t) + idx);
+        v[0] = __uint_as_float(a[0] << 16); v[1] = __uint_as_float(a[0] & 0xffff0000u);
+        v[2] = __uint_as_float(a[1] << 16); v[3] = __uint_as_float(a[1] & 0xffff0000u);
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(t) + idx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = a[e];
+    }
+}
+
 template <int BN, bool TAIL>
 __global__ __launch_bounds__(GT_THREADS, 1) void ctx_kv_tiles(
     const uint16_t* __restrict__ A /*normed [n, Hd]*/, const uint16_t* __restrict__ W /*[N, Hd]*/, int n, int Hd,
     int N, int nM, int ntiles, int Hkv, const uint16_t* __restrict__ k_w /*[L, D]*/, float eps,
-    const int64_t* __restrict__ positions, const float* __restrict__ cos_sin, int64_t max_pos,
-    const int64_t* __restrict__ slots, CtxCaches caches, int64_t num_blocks, int block_size,
+    const int64_t* __restrict__ positions, const void* __restrict__ cos_sin, int rot, bool neox, bool tab_bf16,
+    int64_t max_pos, const int64_t* __restrict__ slots, CtxCaches caches, int64_t num_blocks, int block_size,
     uint16_t* __restrict__ kv_out) {
     constexpr int SP = GT_SP;                // row pitch (floats) of the epilogue staging (one head)
     constexpr int NPASS = BN / CKV_D;        // heads per tile = epilogue passes
@@ -158,51 +182,69 @@ __global__ __launch_bounds__(GT_THREADS, 1) void ctx_kv_tiles(
                 }
                 const float rinv = 1.0f / sqrtf(ss * (1.0f / CKV_D) + eps);
                 const uint16_t* wl = k_w + l * CKV_D;
-                const float* cs = cos_sin + pos * CKV_D;
-                // NeoX pairs (i, i + 64): columns 8c.. and 64 + 8c.. together
-#pragma unroll 2
-                for (int c = 0; c < CKV_D / 16; ++c) {
-                    float x1[8], x2[8], w1[8], w2[8];
+                if (kvo) {  // the row before the norm
+#pragma unroll 4
+                    for (int c = 0; c < CKV_D / 8; ++c) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(rowp + 8 * c);
+                        const f32x4 b = *reinterpret_cast<const f32x4*>(rowp + 8 * c + 4);
+                        stg16(kvo + 8 * c, u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                 pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])});
+                    }
+                }
+                // normed values of columns col .. col + 7
+                auto normed8 = [&](int col, float (&y)[8]) {
+                    float w[8];
+                    unpack8(ldg16(wl + col), w);
 #pragma unroll
                     for (int hq = 0; hq < 2; ++hq) {
-                        const f32x4 a = *reinterpret_cast<const f32x4*>(rowp + 8 * c + 4 * hq);
-                        const f32x4 b = *reinterpret_cast<const f32x4*>(rowp + CKV_D / 2 + 8 * c + 4 * hq);
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(rowp + col + 4 * hq);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            x1[4 * hq + e] = bf16_round(a[e]);
-                            x2[4 * hq + e] = bf16_round(b[e]);
+                        for (int e = 0; e < 4; ++e) y[4 * hq + e] = bf16_round(a[e]) * rinv * w[4 * hq + e];
+                    }
+                };
+                auto put8 = [&](int col, const float (&o)[8]) {
+                    if (dst)
+                        stg16(dst + col, u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                               pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])});
+                };
+                const int half = rot >> 1;
+                const int64_t trow = pos * rot;  // the position's table row: cos(0 .. half), sin(0 .. half)
+                if (neox) {
+                    // pairs (i, i + rot/2): columns 8c.. and rot/2 + 8c.. together
+                    for (int c = 0; c < half / 8; ++c) {
+                        float y1[8], y2[8], cv[8], sv[8], o1[8], o2[8];
+                        normed8(8 * c, y1);
+                        normed8(half + 8 * c, y2);
+                        rope_table8(cos_sin, tab_bf16, trow + 8 * c, cv);
+                        rope_table8(cos_sin, tab_bf16, trow + half + 8 * c, sv);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            o1[e] = y1[e] * cv[e] - y2[e] * sv[e];
+                            o2[e] = y2[e] * cv[e] + y1[e] * sv[e];
                         }
+                        put8(8 * c, o1);
+                        put8(half + 8 * c, o2);
                     }
-                    unpack8(ldg16(wl + 8 * c), w1);
-                    unpack8(ldg16(wl + CKV_D / 2 + 8 * c), w2);
-                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + 8 * c);
-                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 8 * c + 4);
-                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + CKV_D / 2 + 8 * c);
-                    const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + CKV_D / 2 + 8 * c + 4);
-                    const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-                    const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-                    float o1[8], o2[8];
+                } else {
+                    // pairs (2i, 2i + 1): columns 8c.. hold pairs 4c .. 4c + 3
+                    for (int c = 0; c < rot / 8; ++c) {
+                        float y[8], c4[4], s4[4], o[8];
+                        normed8(8 * c, y);
+                        rope_table4(cos_sin, tab_bf16, trow + 4 * c, c4);
+                        rope_table4(cos_sin, tab_bf16, trow + half + 4 * c, s4);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float y1 = x1[e] * rinv * w1[e];
-                        const float y2 = x2[e] * rinv * w2[e];
-                        o1[e] = y1 * cv[e] - y2 * sv[e];
-                        o2[e] = y2 * cv[e] + y1 * sv[e];
+                        for (int m = 0; m < 4; ++m) {
+                            o[2 * m] = y[2 * m] * c4[m] - y[2 * m + 1] * s4[m];
+                            o[2 * m + 1] = y[2 * m + 1] * c4[m] + y[2 * m] * s4[m];
+                        }
+                        put8(8 * c, o);
                     }
-                    if (kvo) {
-                        stg16(kvo + 8 * c, u32x4{pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]),
-                                                 pack_bf16x2(x1[4], x1[5]), pack_bf16x2(x1[6], x1[7])});
-                        stg16(kvo + CKV_D / 2 + 8 * c,
-                              u32x4{pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3]),
-                                    pack_bf16x2(x2[4], x2[5]), pack_bf16x2(x2[6], x2[7])});
-                    }
-                    if (dst) {
-                        stg16(dst + 8 * c, u32x4{pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3]),
-                                                 pack_bf16x2(o1[4], o1[5]), pack_bf16x2(o1[6], o1[7])});
-                        stg16(dst + CKV_D / 2 + 8 * c,
-                              u32x4{pack_bf16x2(o2[0], o2[1]), pack_bf16x2(o2[2], o2[3]),
-                                    pack_bf16x2(o2[4], o2[5]), pack_bf16x2(o2[6], o2[7])});
-                    }
+                }
+                // columns past the rotary dim: the norm alone
+                for (int c = rot / 8; c < CKV_D / 8; ++c) {
+                    float y[8];
+                    normed8(8 * c, y);
+                    put8(8 * c, y);
                 }
             }
         }
@@ -219,12 +261,13 @@ extern "C" size_t dflash_context_kv_workspace_size(int64_t num_ctx, int64_t Hd) 
     return (size_t)num_ctx * (size_t)Hd * 2u;
 }
 
-extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hidden_norm_w, float hidden_eps,
-                                 const uint16_t* W_kv, int64_t num_ctx, int64_t Hd, int32_t L, int32_t Hkv,
-                                 int32_t D, const uint16_t* k_norm_w, float k_eps, const int64_t* positions,
-                                 const float* cos_sin, int64_t max_pos, const int64_t* slots,
-                                 uint16_t* const* caches, int64_t num_blocks, int32_t block_size,
-                                 uint16_t* kv_out, void* ws, size_t ws_bytes, void* stream) {
+extern "C" int dflash_context_kv_ex(const uint16_t* ctx_states, const uint16_t* hidden_norm_w, float hidden_eps,
+                                    const uint16_t* W_kv, int64_t num_ctx, int64_t Hd, int32_t L, int32_t Hkv,
+                                    int32_t D, const uint16_t* k_norm_w, float k_eps, const int64_t* positions,
+                                    const void* cos_sin, int64_t max_pos, int32_t rotary_dim, int32_t is_neox,
+                                    int32_t table_bf16, const int64_t* slots, uint16_t* const* caches,
+                                    int64_t num_blocks, int32_t block_size, uint16_t* kv_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
     const void* req[] = {ctx_states, hidden_norm_w, W_kv, k_norm_w, positions, cos_sin, ws};
     for (const void* p : req)
         if (!p || !DFLASH_ALIGNED16(p)) return DFLASH_ERR_INVALID_ARG;
@@ -232,6 +275,9 @@ extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hid
     if (kv_out && !DFLASH_ALIGNED16(kv_out)) return DFLASH_ERR_INVALID_ARG;
     if (num_ctx < 1 || Hd < 1 || L < 1 || Hkv < 1 || max_pos < 1) return DFLASH_ERR_INVALID_ARG;
     if (!(hidden_eps >= 0.f) || !(k_eps >= 0.f)) return DFLASH_ERR_INVALID_ARG;
+    if ((table_bf16 != 0 && table_bf16 != 1) || (is_neox != 0 && is_neox != 1)) return DFLASH_ERR_INVALID_ARG;
+    if (rotary_dim < 2 || rotary_dim > D || (rotary_dim & 1)) return DFLASH_ERR_INVALID_ARG;
+    if (rotary_dim % (is_neox ? 16 : 8) != 0) return DFLASH_ERR_UNSUPPORTED;
     CtxCaches cp{};
     if (caches) {
         if (num_blocks < 1 || block_size < 1 || L > CKV_MAX_LAYERS) return L > CKV_MAX_LAYERS ? DFLASH_ERR_UNSUPPORTED
@@ -260,7 +306,8 @@ extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hid
     const dim3 grid((unsigned)(8 * per));
 #define CKV_LAUNCH(BNV, TL)                                                                                         \
     hipLaunchKernelGGL((ctx_kv_tiles<BNV, TL>), grid, dim3(GT_THREADS), 0, st, normed, W_kv, (int)num_ctx, (int)Hd, \
-                       (int)N, nM, (int)ntiles, (int)Hkv, k_norm_w, k_eps, positions, cos_sin, max_pos, slots, cp,    \
+                       (int)N, nM, (int)ntiles, (int)Hkv, k_norm_w, k_eps, positions, cos_sin, (int)rotary_dim,       \
+                       is_neox != 0, table_bf16 != 0, max_pos, slots, cp,                                              \
                        num_blocks, (int)block_size, kv_out)
     const bool tail = Hd % GT_BK != 0;
     if (BN == 256) {
@@ -273,4 +320,15 @@ extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hid
 #undef CKV_LAUNCH
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
+}
+
+extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hidden_norm_w, float hidden_eps,
+                                 const uint16_t* W_kv, int64_t num_ctx, int64_t Hd, int32_t L, int32_t Hkv,
+                                 int32_t D, const uint16_t* k_norm_w, float k_eps, const int64_t* positions,
+                                 const float* cos_sin, int64_t max_pos, const int64_t* slots,
+                                 uint16_t* const* caches, int64_t num_blocks, int32_t block_size,
+                                 uint16_t* kv_out, void* ws, size_t ws_bytes, void* stream) {
+    return dflash_context_kv_ex(ctx_states, hidden_norm_w, hidden_eps, W_kv, num_ctx, Hd, L, Hkv, D, k_norm_w, k_eps,
+                                positions, cos_sin, max_pos, D, 1, 0, slots, caches, num_blocks, block_size, kv_out,
+                                ws, ws_bytes, stream);
 }

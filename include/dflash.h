@@ -170,6 +170,13 @@ int dflash_candidate_edges_hp(const uint16_t* pred_cb, const uint16_t* succ_cb,
  * ---------------------------------------------------------------------- */
 int dflash_rope_cos_sin(float* cos_sin, int64_t max_pos, int32_t D, double theta, void* stream);
 
+/* The same table in bf16 (the dtype of the cos/sin cache the pages' fused ops
+ * assert), [max_pos, rotary_dim]: each entry computed in fp64 and rounded to
+ * fp32, then to bf16 (round to nearest even each time).  For the *_ex calls
+ * with table_bf16 = 1.  Requirements as dflash_rope_cos_sin. */
+int dflash_rope_cos_sin_bf16(uint16_t* cos_sin, int64_t max_pos, int32_t rotary_dim, double theta,
+                             void* stream);
+
 /* ------------------------------------------------------------------------
  * Fused per-head q/k RMSNorm + NeoX RoPE + K/V cache write
  * (DFlash2BeamAttention.forward: beam_qk_norm_rope).
@@ -261,6 +268,44 @@ int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hidden_norm_w,
  * ---------------------------------------------------------------------- */
 int dflash_linear(const uint16_t* X, const uint16_t* W, int64_t M, int64_t N, int64_t K,
                   uint16_t* Y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * RoPE options of the fused q/k op and of store_context_kv (both take the
+ * head dim, the rotary dim and is_neox_style; the table the pages pass is a
+ * bf16 cos/sin cache):
+ *
+ * dflash_qk_norm_rope_cache_ex and dflash_context_kv_ex are
+ * dflash_qk_norm_rope_cache and dflash_context_kv with the rotation
+ * generalised; the plain calls are the _ex calls with rotary_dim = D,
+ * is_neox = 1, table_bf16 = 0.
+ *   rotary_dim  the first rotary_dim elements of each head are rotated, the
+ *               rest pass through after the norm; angle index i (i < rotary_dim/2)
+ *               turns by pos * theta^(-2i/rotary_dim)
+ *   is_neox     1: pairs (i, i + rotary_dim/2); 0: pairs (2i, 2i + 1) (GPT-J)
+ *   cos_sin     [max_pos, rotary_dim]: cos of angle index i at column i, sin at
+ *               rotary_dim/2 + i; fp32 (table_bf16 = 0, dflash_rope_cos_sin) or
+ *               bf16 (table_bf16 = 1, dflash_rope_cos_sin_bf16)
+ * Requirements: 2 <= rotary_dim <= D, even (else INVALID_ARG); rotary_dim a
+ * multiple of 16 with is_neox = 1 and of 8 with is_neox = 0 (else UNSUPPORTED);
+ * is_neox, table_bf16 in {0, 1}.  Everything else as in the plain calls.
+ * ---------------------------------------------------------------------- */
+int dflash_qk_norm_rope_cache_ex(const uint16_t* qkv, int64_t row_stride,
+                                 int64_t T_q, int32_t Hq, int32_t Hkv, int32_t D,
+                                 const uint16_t* q_w, const uint16_t* k_w, float eps,
+                                 const int64_t* positions, const void* cos_sin, int64_t max_pos,
+                                 int32_t rotary_dim, int32_t is_neox, int32_t table_bf16,
+                                 const int64_t* slots, uint16_t* kv_cache,
+                                 int64_t num_blocks, int32_t block_size,
+                                 uint16_t* q_out, uint16_t* k_out, void* stream);
+int dflash_context_kv_ex(const uint16_t* ctx_states, const uint16_t* hidden_norm_w, float hidden_eps,
+                         const uint16_t* W_kv, int64_t num_ctx, int64_t Hd,
+                         int32_t L, int32_t Hkv, int32_t D,
+                         const uint16_t* k_norm_w, float k_eps,
+                         const int64_t* positions, const void* cos_sin, int64_t max_pos,
+                         int32_t rotary_dim, int32_t is_neox, int32_t table_bf16,
+                         const int64_t* slots, uint16_t* const* caches,
+                         int64_t num_blocks, int32_t block_size,
+                         uint16_t* kv_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Non-causal sliding-window block attention over a paged cache
