@@ -217,6 +217,9 @@ def main():
                     help="skip the separately timed context K/V precompute (dflash_context_kv)")
     ap.add_argument("--no-draft-layer", action="store_true",
                     help="skip the separately timed draft-layer projections (dflash_linear qkv_proj / o_proj)")
+    ap.add_argument("--no-hbm-regime", action="store_true",
+                    help="skip the LM-head top-k at 256 rows (mid workload; full vocabulary, one position per "
+                         "request), where it is HBM-bound")
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="the oracle baseline runs 1/N of the step's requests (default 4: about 10-20 s on 16 cores)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -419,6 +422,49 @@ def main():
                 "GB_per_s": lb / (l_ms * 1e-3) / 1e9, "algorithmic_bytes": lb, "flops": lf,
                 "workload": f"dflash_linear {Mx} x {Nx} x {Kx} (draft layer {name}; not part of the step)"}
 
+    # the LM-head top-k where it is bandwidth-bound: 256 rows (the mid
+    # workload, and the full vocabulary / hidden size with one position per
+    # request); a 512 MiB scrub write between the timed calls (outside the
+    # events) keeps the weight out of the 256 MB last-level cache
+    hbm_kernels = {}
+    if not args.no_hbm_regime:
+        log("LM-head top-k at 256 rows ...")
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        mid = WL.candidate_inputs("mid")
+        cases = [("lm_topk_mid", dbf(mid["H"]), dbf(mid["W"]), mid["top_k"], mid["multiplier"], mid["softcap"],
+                  "mid workload: 256 rows (32 requests x 8 steps), vocab 32768, hidden 2048, top_k 8, softcap 30"),
+                 ("lm_topk_full_vocab_256_rows", H[:256].contiguous(), W, k, cand["multiplier"], cand["softcap"],
+                  "256 rows (one position of 256 requests), vocab 151936, hidden 4096, top_k 16, multiplier 0.5, "
+                  "softcap 30")]
+        for name, Hx, Wx, kx, sx, cx, desc in cases:
+            Tx, Hdx = Hx.shape
+            Vx = Wx.shape[0]
+            idsx = torch.empty((Tx, kx), dtype=torch.int32, device=dev)
+            lgx = torch.empty((Tx, kx), dtype=torch.float32, device=dev)
+            wsx = torch.empty(max(16, B.lm_topk_workspace_size(Tx, Vx, Hdx, kx)), dtype=torch.uint8, device=dev)
+            for _ in range(args.warmup):
+                B.lm_topk(Hx, Wx, kx, sx, cx, idsx, lgx, wsx)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            tms = []
+            for _ in range(max(args.steps // 2, 5)):
+                scrub.fill_(1)
+                e0.record()
+                B.lm_topk(Hx, Wx, kx, sx, cx, idsx, lgx, wsx)
+                e1.record()
+                torch.cuda.synchronize()
+                tms.append(e0.elapsed_time(e1))
+            tms.sort()
+            ms = tms[len(tms) // 2]
+            xb, xf = lm_bytes(Tx, Vx, Hdx, kx), lm_flops(Tx, Vx, Hdx)
+            floor_ms = max(xb / (HBM_PEAK_GBS * 1e9), xf / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+            hbm_kernels[name] = {
+                "ms": ms, "GB_per_s": xb / (ms * 1e-3) / 1e9, "hbm_frac": xb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "TFLOP_per_s": xf / (ms * 1e-3) / 1e12,
+                "mfma_frac": xf / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "binding_roofline_frac": floor_ms / ms, "algorithmic_bytes": xb, "flops": xf,
+                "workload": desc + " (median of the timed calls, cache scrubbed before each; not part of the step)"}
+        del scrub
+
     result = {
         "metric": METRIC,
         "value": value,
@@ -474,6 +520,7 @@ def main():
     if ctx_kernel is not None:
         result["kernels"]["context_kv"] = ctx_kernel
     result["kernels"].update(lin_kernels)
+    result["kernels"].update(hbm_kernels)
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(cand, attn, edges_per_step, args.cpu_sample)

@@ -20,7 +20,8 @@
 //   * Row slices and groups are blocked per XCD (workgroup ids go to XCDs
 //     round-robin), so each XCD's L2 serves W tiles to several row slices and
 //     H slices to several groups.
-//   * A merge kernel picks the k best of the groups' partial lists per row.
+//   * A merge kernel picks the k best of the groups' partial lists per row
+//     (with more than 16 groups, after levels that merge blocks of 16 lists).
 #include "common.h"
 
 namespace dflash {
@@ -469,51 +470,6 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     }
 }
 
-// One wave per row: k best of the row's G * KCAP partial entries
-// (entry = ordered key << 32 | ~id; larger is better; 0 = empty).
-template <int KCAP>
-__global__ __launch_bounds__(256) void lm_topk_merge(const uint64_t* __restrict__ part, int T, int G,
-                                                     int k, int32_t* __restrict__ ids,
-                                                     float* __restrict__ logits) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= T) return;
-    const int n = G * KCAP;
-    const uint64_t* src = part + (int64_t)row * n;
-    uint64_t Ls[KCAP];
-#pragma unroll
-    for (int j = 0; j < KCAP; ++j) Ls[j] = 0;
-    for (int i = lane; i < n; i += 64) {
-        const uint64_t p = src[i];
-        if (p > Ls[KCAP - 1]) {
-#pragma unroll
-            for (int j = KCAP - 1; j > 0; --j) {
-                const uint64_t lo = Ls[j - 1] < p ? Ls[j - 1] : p;
-                Ls[j] = Ls[j] > lo ? Ls[j] : lo;
-            }
-            Ls[0] = Ls[0] > p ? Ls[0] : p;
-        }
-    }
-    for (int r = 0; r < k; ++r) {
-        uint64_t best = Ls[0];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const uint64_t o = __shfl_xor(best, off);
-            best = o > best ? o : best;
-        }
-        if (Ls[0] == best && best != 0) {
-#pragma unroll
-            for (int j = 0; j < KCAP - 1; ++j) Ls[j] = Ls[j + 1];
-            Ls[KCAP - 1] = 0;
-        }
-        if (lane == 0) {
-            const uint32_t okey = (uint32_t)(best >> 32);
-            ids[(int64_t)row * k + r] = (int32_t)(~(uint32_t)best);
-            logits[(int64_t)row * k + r] = best ? bf16_bits_to_f32(unorder_key(okey)) : -INFINITY;
-        }
-    }
-}
-
 // Merge for G <= 16 groups: 16 lanes per row (four rows per wave), lane g
 // holding group g's sorted list in registers.  Each round takes the largest
 // head over the 16 lanes (DPP row rotations, no LDS round trip) and the lane
@@ -564,6 +520,43 @@ __global__ __launch_bounds__(256) void lm_topk_merge16(const uint64_t* __restric
     }
 }
 
+// One level of the merge for G > 16 groups: the same 16-lane rounds over
+// blocks of 16 groups, a "virtual row" per (row, block), writing the block's
+// KCAP best entries as one partial list: [T, G, KCAP] -> [T, ceil(G/16), KCAP].
+// Any strict total order keeps the global top k inside the union of the
+// blocks' top-KCAP lists, so levels compose until G <= 16.
+template <int KCAP>
+__global__ __launch_bounds__(256) void lm_topk_merge16_level(const uint64_t* __restrict__ part, int T, int G,
+                                                             int G2, uint64_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t vrow = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const int64_t row = vrow / G2;
+    const int blk = (int)(vrow - row * G2);
+    const int g = blk * 16 + (lane & 15);
+    uint64_t L[KCAP];
+    if (row < T && g < G) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(part + (row * G + g) * KCAP);
+#pragma unroll
+        for (int j = 0; j < KCAP / 2; ++j) {
+            const u32x4 v = src[j];
+            L[2 * j] = ((uint64_t)v[1] << 32) | v[0];
+            L[2 * j + 1] = ((uint64_t)v[3] << 32) | v[2];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KCAP; ++j) L[j] = 0;
+    }
+    for (int r = 0; r < KCAP; ++r) {
+        const uint64_t best = row16_max(L[0]);
+        if (best != 0 && L[0] == best) {
+#pragma unroll
+            for (int j = 0; j < KCAP - 1; ++j) L[j] = L[j + 1];
+            L[KCAP - 1] = 0;
+        }
+        if ((lane & 15) == 0 && row < T) out[(row * G2 + blk) * KCAP + r] = best;
+    }
+}
+
 struct LmPlan {
     int BN, KCAP, nM, nN, G, xmx;
     int64_t nwg;
@@ -604,7 +597,10 @@ static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p) {
         }
         if (best > 0 && (p.G / (per / best)) * (p.nM / best) == 8) p.xmx = best;
     }
-    p.ws = (size_t)T * (size_t)p.G * (size_t)p.KCAP * sizeof(uint64_t);
+    // partial lists, plus two ping-pong buffers for the merge levels of G > 16
+    const size_t lists = (size_t)T * (size_t)p.G * (size_t)p.KCAP * sizeof(uint64_t);
+    const size_t level = p.G > 16 ? (size_t)T * (size_t)((p.G + 15) / 16) * (size_t)p.KCAP * sizeof(uint64_t) : 0;
+    p.ws = lists + 2 * level;
     return true;
 }
 
@@ -636,12 +632,23 @@ static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, in
         launch_tiles<256, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
     else
         launch_tiles<128, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
-    if (p.G <= 16)
-        hipLaunchKernelGGL((lm_topk_merge16<KCAP>), dim3((T + 15) / 16), dim3(256), 0, st, part, T, p.G, k, ids,
-                           logits);
-    else
-        hipLaunchKernelGGL((lm_topk_merge<KCAP>), dim3((T + 3) / 4), dim3(256), 0, st, part, T, p.G, k, ids,
-                           logits);
+    const uint64_t* cur = part;
+    int G = p.G;
+    if (G > 16) {
+        // levels of 16 -> 1 until 16 or fewer lists per row remain
+        uint64_t* buf[2];
+        buf[0] = part + (size_t)T * (size_t)p.G * KCAP;
+        buf[1] = buf[0] + (size_t)T * (size_t)((p.G + 15) / 16) * KCAP;
+        for (int lv = 0; G > 16; ++lv) {
+            const int G2 = (G + 15) / 16;
+            const int64_t vrows = (int64_t)T * G2;
+            hipLaunchKernelGGL((lm_topk_merge16_level<KCAP>), dim3((unsigned)((vrows + 15) / 16)), dim3(256), 0, st,
+                               cur, T, G, G2, buf[lv & 1]);
+            cur = buf[lv & 1];
+            G = G2;
+        }
+    }
+    hipLaunchKernelGGL((lm_topk_merge16<KCAP>), dim3((T + 15) / 16), dim3(256), 0, st, cur, T, G, k, ids, logits);
 }
 
 }  // namespace dflash
