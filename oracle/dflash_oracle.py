@@ -49,7 +49,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "f64_to_f32", "lm_logit_keys", "lm_topk",
     "candidate_edges", "qk_norm_rope_cache", "block_attn", "attention_window",
     "rank_projection", "candidate_edges_from_hp", "rms_norm", "context_kv", "store_context_kv",
-    "linear", "draft_attention", "rope_cos_sin",
+    "linear", "draft_attention", "rope_cos_sin", "fp8_to_f64", "f64_to_fp8", "bf16_to_fp8_scaled",
 ]
 
 
@@ -81,6 +81,64 @@ def f32_to_bf16(x32: np.ndarray) -> np.ndarray:
 def f64_to_bf16(x: np.ndarray) -> np.ndarray:
     """float64 -> fp32 -> bf16 bits (each step round to nearest even)."""
     return f32_to_bf16(f64_to_f32(x))
+
+
+# --------------------------------------------------------------------------
+# fp8 (OCP E4M3 "fn" and E5M2), for fp8 K/V caches
+# --------------------------------------------------------------------------
+FP8_FORMATS = {
+    # name: (exponent bits, mantissa bits, bias, no-infinity "fn" variant)
+    "e4m3": (4, 3, 7, True),    # float8_e4m3fn: S.1111.111 is NaN, no inf, max 448
+    "e5m2": (5, 2, 15, False),  # float8_e5m2: IEEE-like, S.11111.00 = inf, max 57344
+}
+
+
+def fp8_to_f64(codes, fmt: str) -> np.ndarray:
+    """Decode fp8 codes (uint8) by the format's definition: exponent field 0 is
+    subnormal (m * 2^(1 - bias - mbits)), else (1 + m / 2^mbits) * 2^(e - bias)."""
+    eb, mb, bias, fn = FP8_FORMATS[fmt]
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sgn = (c >> 7) & 1
+    e = (c >> mb) & ((1 << eb) - 1)
+    m = c & ((1 << mb) - 1)
+    val = np.where(e == 0, m * 2.0 ** (1 - bias - mb), (1.0 + m / 2.0 ** mb) * 2.0 ** (e - bias))
+    emax = (1 << eb) - 1
+    if fn:
+        val = np.where((e == emax) & (m == (1 << mb) - 1), np.nan, val)
+    else:
+        val = np.where(e == emax, np.where(m == 0, np.inf, np.nan), val)
+    return np.where(sgn == 1, -val, val)
+
+
+def _fp8_positive_table(fmt: str):
+    codes = np.arange(128, dtype=np.uint8)
+    vals = fp8_to_f64(codes, fmt)
+    ok = np.isfinite(vals)
+    return codes[ok], vals[ok]  # ascending in both
+
+
+def f64_to_fp8(x, fmt: str) -> np.ndarray:
+    """Round to the nearest finite fp8 value (ties to the even code), saturating
+    at the largest finite magnitude; NaN -> the NaN code.  Brute force over the
+    format's finite values."""
+    codes, vals = _fp8_positive_table(fmt)
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    i = np.clip(np.searchsorted(vals, a), 1, len(vals) - 1)
+    lo, hi = vals[i - 1], vals[i]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & (codes[i] % 2 == 0))
+    c = np.where(pick_hi, codes[i], codes[i - 1])
+    c = np.where(a >= vals[-1], codes[-1], c)
+    c = np.where(a <= 0, 0, c)
+    c = c.astype(np.uint8) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), c).astype(np.uint8)
+
+
+def bf16_to_fp8_scaled(bits, scale: float, fmt: str) -> np.ndarray:
+    """Cache code of a bf16 value under a per-layer scale: the value divided by
+    the scale in fp32 (one IEEE rounding), then ``f64_to_fp8``."""
+    q = bf16_to_f64(bits).astype(np.float32) / np.float32(scale)
+    return f64_to_fp8(q.astype(np.float64), fmt)
 
 
 # --------------------------------------------------------------------------
@@ -241,7 +299,8 @@ def _rope(y: np.ndarray, c: np.ndarray, s: np.ndarray, neox: bool) -> np.ndarray
 def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float,
                        positions, theta: float, slots=None, cache=None,
                        block_size: int = 16, rotary_dim: int | None = None,
-                       neox: bool = True, table: str = "f64"):
+                       neox: bool = True, table: str = "f64",
+                       cache_fp8: str | None = None, k_scale: float = 1.0, v_scale: float = 1.0):
     """Draft layer's fused q/k norm + RoPE + cache write.
 
     ``qkv``: bf16 ``[T, (Hq + 2 Hkv) D]``, q heads, then k heads, then v heads.
@@ -251,7 +310,9 @@ def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float,
     ``neox=False``; cos/sin as ``rope_cos_sin(..., table)``), one bf16
     rounding at the output.  With a cache, token t with ``slots[t] >= 0``
     writes K' to ``cache[slot // bs, h, slot % bs, :D]`` and its V bits
-    unchanged to ``[..., D:]``; negative slots write nothing.
+    unchanged to ``[..., D:]``; negative slots write nothing.  With
+    ``cache_fp8`` the cache is uint8 and holds ``bf16_to_fp8_scaled`` of k_out
+    and of V (what an attention backend stores from the layer's bf16 k and v).
 
     Returns ``(q_out bf16 [T,Hq,D], k_out bf16 [T,Hkv,D], cache_out or None)``.
     """
@@ -268,12 +329,16 @@ def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float,
     if cache is not None and slots is not None:
         cache_out = np.array(cache, copy=True)
         v_bits = qkv.reshape(T, Hq + 2 * Hkv, D)[:, Hq + Hkv:]
+        k_store = k_out
+        if cache_fp8 is not None:
+            k_store = bf16_to_fp8_scaled(k_out, k_scale, cache_fp8)
+            v_bits = bf16_to_fp8_scaled(v_bits, v_scale, cache_fp8)
         for t in range(T):
             s = int(slots[t])
             if s < 0:
                 continue
             b, o = divmod(s, block_size)
-            cache_out[b, :, o, :D] = k_out[t]
+            cache_out[b, :, o, :D] = k_store[t]
             cache_out[b, :, o, D:] = v_bits[t]
     return q_out, k_out, cache_out
 
@@ -301,7 +366,8 @@ def context_kv(context_states, hidden_norm_w, eps: float, W_ctx, L: int, Hkv: in
 
 
 def store_context_kv(kv, k_norm_w, eps: float, positions, theta: float, slots, caches, block_size: int = 16,
-                     rotary_dim: int | None = None, neox: bool = True, table: str = "f64"):
+                     rotary_dim: int | None = None, neox: bool = True, table: str = "f64",
+                     cache_fp8: str | None = None, k_scale=None, v_scale=None):
     """``store_context_kv``: for every layer l at once, K = the layer's K-norm
     (weights ``k_norm_w[l]``) and NeoX RoPE at the context token's position (the
     keys the drafter's queries attend to carry both, like its own keys), one
@@ -311,8 +377,11 @@ def store_context_kv(kv, k_norm_w, eps: float, positions, theta: float, slots, c
 
     ``kv`` bf16 ``[num_ctx, L, 2, Hkv, D]``; ``k_norm_w`` bf16 ``[L, D]``;
     ``caches`` a list of L bf16 arrays ``[blocks, Hkv, bs, 2D]``.  The RoPE
-    options are those of ``qk_norm_rope_cache``.  Returns the list of updated
-    caches.
+    options are those of ``qk_norm_rope_cache``.  With ``cache_fp8`` ("e4m3" or
+    "e5m2") the caches are uint8 ``[blocks, Hkv, bs, 2D]`` and layer l stores
+    ``bf16_to_fp8_scaled`` of its bf16 K' and V under ``k_scale[l]`` /
+    ``v_scale[l]`` (reading: the value quantised is the one the bf16 cache would
+    hold).  Returns the list of updated caches.
     """
     kv = np.asarray(kv)
     n, L, _, Hkv, D = kv.shape
@@ -322,13 +391,17 @@ def store_context_kv(kv, k_norm_w, eps: float, positions, theta: float, slots, c
     for l in range(L):
         k = _rope(_rms_norm(bf16_to_f64(kv[:, l, 0]), bf16_to_f64(k_norm_w[l]), eps), c, s, neox)
         k_bits = f64_to_bf16(k)
+        v_bits = kv[:, l, 1]
+        if cache_fp8 is not None:
+            k_bits = bf16_to_fp8_scaled(k_bits, float(k_scale[l]), cache_fp8)
+            v_bits = bf16_to_fp8_scaled(v_bits, float(v_scale[l]), cache_fp8)
         for t in range(n):
             slot = int(slots[t])
             if slot < 0:
                 continue
             b, o = divmod(slot, block_size)
             out[l][b, :, o, :D] = k_bits[t]
-            out[l][b, :, o, D:] = kv[t, l, 1]
+            out[l][b, :, o, D:] = v_bits[t]
     return out
 
 
@@ -348,10 +421,13 @@ def attention_window(seq_len: int, Lq: int, i: int, window: int):
 
 
 def block_attn(q, cache, block_tables, seq_lens, Lq: int, Hq: int, Hkv: int,
-               D: int, block_size: int, window: int, scale: float) -> np.ndarray:
+               D: int, block_size: int, window: int, scale: float,
+               cache_fp8: str | None = None, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """``o = softmax(q K^T * scale) V`` per (request, q head, query), float64,
     over the visible keys (``attention_window``), K/V gathered through the
     block table; kv head = q head // (Hq / Hkv).  Output bf16 ``[Rq*Lq, Hq, D]``.
+    With ``cache_fp8`` the cache holds fp8 codes: K = code value * k_scale,
+    V = code value * v_scale.
     """
     Rq = len(seq_lens)
     group = Hq // Hkv
@@ -363,8 +439,12 @@ def block_attn(q, cache, block_tables, seq_lens, Lq: int, Hq: int, Hkv: int,
         kpos = np.arange(lo0, L)
         phys = np.asarray(block_tables[r])[kpos // block_size]
         rows = cache[phys, :, kpos % block_size, :]            # [nk, Hkv, 2D]
-        Kf = bf16_to_f64(rows[:, :, :D])
-        Vf = bf16_to_f64(rows[:, :, D:])
+        if cache_fp8 is None:
+            Kf = bf16_to_f64(rows[:, :, :D])
+            Vf = bf16_to_f64(rows[:, :, D:])
+        else:
+            Kf = fp8_to_f64(rows[:, :, :D], cache_fp8) * k_scale
+            Vf = fp8_to_f64(rows[:, :, D:], cache_fp8) * v_scale
         visible = np.zeros((Lq, len(kpos)), dtype=bool)       # [query, key]
         for i in range(Lq):
             lo, hi = attention_window(L, Lq, i, window)
