@@ -40,10 +40,10 @@ _SIGS = {
     "dflash_rope_cos_sin_bf16": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_f64, _c_p]),
     "dflash_qk_norm_rope_cache_ex": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
                                                     _c_f32, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
-                                                    _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+                                                    _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
     "dflash_context_kv_ex": (ctypes.c_int, [_c_p, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                             _c_p, _c_f32, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
-                                            _c_i64, _c_i32, _c_p, _c_p, _c_sz, _c_p]),
+                                            _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dflash_qk_norm_rope_cache": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
                                                  _c_f32, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32,
                                                  _c_p, _c_p, _c_p]),
@@ -226,6 +226,21 @@ def rope_cos_sin(max_pos: int, D: int, theta: float, device, out=None, stream=No
     return out
 
 
+FP8_CODES = {None: 0, "e4m3": 1, "e5m2": 2}
+
+
+def _cache_args(cache_fp8, scales, n_scales):
+    """(format code, scales pointer) of the fp8 cache options; fp8 caches are
+    torch.uint8 tensors and the scales a device fp32 tensor of n_scales."""
+    if cache_fp8 not in FP8_CODES:
+        raise ValueError("cache_fp8 must be None, 'e4m3' or 'e5m2'")
+    if cache_fp8 is None:
+        return 0, None
+    if scales is None or scales.numel() != n_scales:
+        raise ValueError(f"an fp8 cache needs {n_scales} scales")
+    return FP8_CODES[cache_fp8], _dev(scales, torch.float32, "kv_scale")
+
+
 def _rope_args(cos_sin, D, rotary_dim, is_neox):
     """(pointer, rotary_dim, is_neox, table_bf16) of a RoPE table argument."""
     rot = D if rotary_dim is None else int(rotary_dim)
@@ -237,7 +252,8 @@ def _rope_args(cos_sin, D, rotary_dim, is_neox):
 
 def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, positions, cos_sin,
                        slots=None, kv_cache=None, q_out=None, k_out=None, want_k: bool = True,
-                       stream=None, rotary_dim: int | None = None, is_neox: bool = True):
+                       stream=None, rotary_dim: int | None = None, is_neox: bool = True,
+                       cache_fp8: str | None = None, kv_scale=None):
     """Fused per-head RMSNorm + NeoX RoPE of the q and k heads of ``qkv``
     ``[T, >= (Hq + 2 Hkv) D]`` (bf16), writing K/V into ``kv_cache`` at
     ``slots`` when both are given.  Returns ``(q_out, k_out or None)``."""
@@ -256,12 +272,14 @@ def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, pos
     if qkv.dtype != torch.bfloat16 or not qkv.is_cuda:
         raise TypeError("qkv must be a bf16 device tensor")
     cs_ptr, rot, neox, tbf = _rope_args(cos_sin, D, rotary_dim, is_neox)
+    f8, sc = _cache_args(cache_fp8, kv_scale, 2)
+    cache_dtype = torch.uint8 if f8 else torch.bfloat16
     st = lib().dflash_qk_norm_rope_cache_ex(
         qkv.data_ptr(), qkv.stride(0), T, Hq, Hkv, D, _dev(q_w, torch.bfloat16, "q_w"),
         _dev(k_w, torch.bfloat16, "k_w"), float(eps), _dev(positions, torch.int64, "positions"),
         cs_ptr, cos_sin.shape[0], rot, neox, tbf,
         None if slots is None else _dev(slots, torch.int64, "slots"),
-        None if kv_cache is None else _dev(kv_cache, torch.bfloat16, "kv_cache"), nblk, bs,
+        None if kv_cache is None else _dev(kv_cache, cache_dtype, "kv_cache"), nblk, bs, f8, sc,
         _dev(q_out, torch.bfloat16, "q_out"), None if k_out is None else _dev(k_out, torch.bfloat16, "k_out"),
         _stream(stream))
     _check(st, "dflash_qk_norm_rope_cache_ex")
@@ -299,7 +317,8 @@ def context_kv_workspace_size(num_ctx: int, Hd: int) -> int:
 
 def context_kv(ctx_states, hidden_norm_w, hidden_eps: float, W_kv, L: int, Hkv: int, D: int, k_norm_w,
                k_eps: float, positions, cos_sin, slots=None, caches=None, kv_out=None, want_kv: bool = False,
-               workspace=None, stream=None, rotary_dim: int | None = None, is_neox: bool = True):
+               workspace=None, stream=None, rotary_dim: int | None = None, is_neox: bool = True,
+               cache_fp8: str | None = None, kv_scales=None):
     """Context K/V of every draft layer: ``hidden_norm`` of ``ctx_states
     [num_ctx, Hd]`` (bf16), the stacked K/V linear ``W_kv [L*2*Hkv*D, Hd]``,
     then each layer's K-norm (``k_norm_w [L, D]``) + NeoX RoPE and the write of
@@ -323,16 +342,18 @@ def context_kv(ctx_states, hidden_norm_w, hidden_eps: float, W_kv, L: int, Hkv: 
         for c in caches:
             if c.shape != (nblk, Hkv, bs, 2 * D):
                 raise ValueError("every cache must be [num_blocks, Hkv, block_size, 2D]")
-        ptrs = (ctypes.c_void_p * L)(*[_dev(c, torch.bfloat16, "cache") for c in caches])
+        ptrs = (ctypes.c_void_p * L)(*[_dev(c, torch.uint8 if cache_fp8 else torch.bfloat16, "cache")
+                                       for c in caches])
     ws = _workspace(context_kv_workspace_size(n, Hd), dev, workspace)
     cs_ptr, rot, neox, tbf = _rope_args(cos_sin, D, rotary_dim, is_neox)
+    f8, sc = _cache_args(cache_fp8, kv_scales, 2 * L)
     st = lib().dflash_context_kv_ex(
         _dev(ctx_states, torch.bfloat16, "ctx_states"), _dev(hidden_norm_w, torch.bfloat16, "hidden_norm_w"),
         float(hidden_eps), _dev(W_kv, torch.bfloat16, "W_kv"), n, Hd, L, Hkv, D,
         _dev(k_norm_w, torch.bfloat16, "k_norm_w"), float(k_eps), _dev(positions, torch.int64, "positions"),
         cs_ptr, cos_sin.shape[0], rot, neox, tbf,
         None if slots is None else _dev(slots, torch.int64, "slots"),
-        None if ptrs is None else ctypes.cast(ptrs, ctypes.c_void_p), nblk, bs,
+        None if ptrs is None else ctypes.cast(ptrs, ctypes.c_void_p), nblk, bs, f8, sc,
         None if kv_out is None else _dev(kv_out, torch.bfloat16, "kv_out"),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "dflash_context_kv_ex")

@@ -23,6 +23,7 @@
 //     unless the caller asks for it.
 //   * Tiles are dealt to XCDs in contiguous runs (row tiles fastest), so the
 //     workgroups of an XCD share weight tiles and context slices in its L2.
+#include "fp8.h"
 #include "gemm_tile.h"
 
 namespace dflash {
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(GT_THREADS, 1) void ctx_kv_tiles(
     int N, int nM, int ntiles, int Hkv, const uint16_t* __restrict__ k_w /*[L, D]*/, float eps,
     const int64_t* __restrict__ positions, const void* __restrict__ cos_sin, int rot, bool neox, bool tab_bf16,
     int64_t max_pos, const int64_t* __restrict__ slots, CtxCaches caches, int64_t num_blocks, int block_size,
-    uint16_t* __restrict__ kv_out) {
+    uint16_t* __restrict__ kv_out, int fp8, const float* __restrict__ kv_scales) {
     constexpr int SP = GT_SP;                // row pitch (floats) of the epilogue staging (one head)
     constexpr int NPASS = BN / CKV_D;        // heads per tile = epilogue passes
     static_assert(BN % CKV_D == 0, "tiles hold whole heads");
@@ -157,7 +158,24 @@ __global__ __launch_bounds__(GT_THREADS, 1) void ctx_kv_tiles(
             const int h = is_v ? r - Hkv : r;
             const float* rowp = stage + tid * SP;
             uint16_t* kvo = kv_out != nullptr ? kv_out + (int64_t)my_row * N + gh * CKV_D : nullptr;
-            uint16_t* dst = cache_row >= 0 ? caches.p[l] + cache_row + h * head_stride + (is_v ? CKV_D : 0) : nullptr;
+            // the row's place in the layer's cache: bf16 elements, or fp8 bytes
+            // (the same element offsets) when the cache is fp8
+            uint16_t* dst = nullptr;
+            uint8_t* dst8 = nullptr;
+            if (cache_row >= 0) {
+                const int64_t off = cache_row + h * head_stride + (is_v ? CKV_D : 0);
+                if (fp8 == FP8_NONE) dst = caches.p[l] + off;
+                else dst8 = reinterpret_cast<uint8_t*>(caches.p[l]) + off;
+            }
+            const float qscale = fp8 == FP8_NONE ? 1.f : kv_scales[2 * l + (is_v ? 1 : 0)];
+            // 8 values (already bf16 numbers) at column col of the fp8 row
+            auto put8_fp8 = [&](int col, const float (&o)[8]) {
+                float ob[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ob[e] = bf16_round(o[e]);
+                const u32x2 w = fp8 == FP8_E4M3 ? pack_fp8x8<FP8_E4M3>(ob, qscale) : pack_fp8x8<FP8_E5M2>(ob, qscale);
+                *reinterpret_cast<u32x2*>(dst8 + col) = w;
+            };
             if (is_v) {
 #pragma unroll 4
                 for (int c = 0; c < CKV_D / 8; ++c) {
@@ -167,6 +185,10 @@ __global__ __launch_bounds__(GT_THREADS, 1) void ctx_kv_tiles(
                                      pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
                     if (kvo) stg16(kvo + 8 * c, o);
                     if (dst) stg16(dst + 8 * c, o);
+                    if (dst8) {
+                        const float ov[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                        put8_fp8(8 * c, ov);
+                    }
                 }
             } else {
                 // the linear's bf16 output, then the layer's K RMSNorm over the head
@@ -206,6 +228,7 @@ __global__ __launch_bounds__(GT_THREADS, 1) void ctx_kv_tiles(
                     if (dst)
                         stg16(dst + col, u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
                                                pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])});
+                    if (dst8) put8_fp8(col, o);
                 };
                 const int half = rot >> 1;
                 const int64_t trow = pos * rot;  // the position's table row: cos(0 .. half), sin(0 .. half)
@@ -266,8 +289,9 @@ extern "C" int dflash_context_kv_ex(const uint16_t* ctx_states, const uint16_t* 
                                     int32_t D, const uint16_t* k_norm_w, float k_eps, const int64_t* positions,
                                     const void* cos_sin, int64_t max_pos, int32_t rotary_dim, int32_t is_neox,
                                     int32_t table_bf16, const int64_t* slots, uint16_t* const* caches,
-                                    int64_t num_blocks, int32_t block_size, uint16_t* kv_out, void* ws,
-                                    size_t ws_bytes, void* stream) {
+                                    int64_t num_blocks, int32_t block_size, int32_t cache_fp8,
+                                    const float* kv_scales, uint16_t* kv_out, void* ws, size_t ws_bytes,
+                                    void* stream) {
     const void* req[] = {ctx_states, hidden_norm_w, W_kv, k_norm_w, positions, cos_sin, ws};
     for (const void* p : req)
         if (!p || !DFLASH_ALIGNED16(p)) return DFLASH_ERR_INVALID_ARG;
@@ -278,6 +302,8 @@ extern "C" int dflash_context_kv_ex(const uint16_t* ctx_states, const uint16_t* 
     if ((table_bf16 != 0 && table_bf16 != 1) || (is_neox != 0 && is_neox != 1)) return DFLASH_ERR_INVALID_ARG;
     if (rotary_dim < 2 || rotary_dim > D || (rotary_dim & 1)) return DFLASH_ERR_INVALID_ARG;
     if (rotary_dim % (is_neox ? 16 : 8) != 0) return DFLASH_ERR_UNSUPPORTED;
+    if (cache_fp8 < FP8_NONE || cache_fp8 > FP8_E5M2) return DFLASH_ERR_INVALID_ARG;
+    if (cache_fp8 != FP8_NONE && (!caches || !kv_scales || !DFLASH_ALIGNED16(kv_scales))) return DFLASH_ERR_INVALID_ARG;
     CtxCaches cp{};
     if (caches) {
         if (num_blocks < 1 || block_size < 1 || L > CKV_MAX_LAYERS) return L > CKV_MAX_LAYERS ? DFLASH_ERR_UNSUPPORTED
@@ -308,7 +334,7 @@ extern "C" int dflash_context_kv_ex(const uint16_t* ctx_states, const uint16_t* 
     hipLaunchKernelGGL((ctx_kv_tiles<BNV, TL>), grid, dim3(GT_THREADS), 0, st, normed, W_kv, (int)num_ctx, (int)Hd, \
                        (int)N, nM, (int)ntiles, (int)Hkv, k_norm_w, k_eps, positions, cos_sin, (int)rotary_dim,       \
                        is_neox != 0, table_bf16 != 0, max_pos, slots, cp,                                              \
-                       num_blocks, (int)block_size, kv_out)
+                       num_blocks, (int)block_size, kv_out, (int)cache_fp8, kv_scales)
     const bool tail = Hd % GT_BK != 0;
     if (BN == 256) {
         if (tail) CKV_LAUNCH(256, true);
@@ -329,6 +355,6 @@ extern "C" int dflash_context_kv(const uint16_t* ctx_states, const uint16_t* hid
                                  uint16_t* const* caches, int64_t num_blocks, int32_t block_size,
                                  uint16_t* kv_out, void* ws, size_t ws_bytes, void* stream) {
     return dflash_context_kv_ex(ctx_states, hidden_norm_w, hidden_eps, W_kv, num_ctx, Hd, L, Hkv, D, k_norm_w, k_eps,
-                                positions, cos_sin, max_pos, D, 1, 0, slots, caches, num_blocks, block_size, kv_out,
-                                ws, ws_bytes, stream);
+                                positions, cos_sin, max_pos, D, 1, 0, slots, caches, num_blocks, block_size,
+                                FP8_NONE, nullptr, kv_out, ws, ws_bytes, stream);
 }

@@ -11,7 +11,7 @@
 // reduced inside the 16-lane group, and the RoPE partner (i <-> i + 64) of a
 // lane's 8 elements lives in lane ^ 8 of the same group.  V heads are copied to
 // the cache bit for bit.
-#include "common.h"
+#include "fp8.h"
 
 namespace dflash {
 
@@ -82,13 +82,14 @@ __device__ __forceinline__ void lane_rope_coeffs(const void* table, int64_t pos,
     }
 }
 
-template <bool NEOX, bool TBF16>
+template <bool NEOX, bool TBF16, int FP8>
 __global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
     const uint16_t* __restrict__ qkv, int64_t row_stride, int Hq, int Hkv,
     const uint16_t* __restrict__ q_w, const uint16_t* __restrict__ k_w, float eps,
     const int64_t* __restrict__ positions, const void* __restrict__ cos_sin, int rot,
     int64_t max_pos, const int64_t* __restrict__ slots, uint16_t* __restrict__ cache, int64_t num_blocks,
-    int block_size, uint16_t* __restrict__ q_out, uint16_t* __restrict__ k_out) {
+    int block_size, uint16_t* __restrict__ q_out, uint16_t* __restrict__ k_out,
+    const float* __restrict__ kv_scale) {
     const int NH = Hq + 2 * Hkv;
     const int64_t t = blockIdx.x;
     const int grp = threadIdx.x >> 4;
@@ -124,8 +125,18 @@ __global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
         for (int i = 0; i < QK_HPG; ++i) {
             const int h = h0 + 16 * i;
             if (h >= NH) break;  // uniform within the 16-lane group
-            if (h >= Hq + Hkv) {  // v head: copied as is
-                if (cache_base >= 0) stg16(cache + cache_base + (h - Hq - Hkv) * head_stride + QK_D + j * 8, raw[i]);
+            if (h >= Hq + Hkv) {  // v head: copied as is (an fp8 cache: quantised)
+                if (cache_base >= 0) {
+                    const int64_t off = cache_base + (h - Hq - Hkv) * head_stride + QK_D + j * 8;
+                    if (FP8 == FP8_NONE) {
+                        stg16(cache + off, raw[i]);
+                    } else {
+                        float v[8];
+                        unpack8(raw[i], v);
+                        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(cache) + off) =
+                            pack_fp8x8<FP8>(v, kv_scale[1]);
+                    }
+                }
                 continue;
             }
             float x[8];
@@ -157,7 +168,17 @@ __global__ __launch_bounds__(256) void qk_norm_rope_cache_kernel(
             } else {
                 const int hk = h - Hq;
                 if (k_out != nullptr) stg16(k_out + (t * Hkv + hk) * QK_D + j * 8, packed);
-                if (cache_base >= 0) stg16(cache + cache_base + hk * head_stride + j * 8, packed);
+                if (cache_base >= 0) {
+                    const int64_t off = cache_base + hk * head_stride + j * 8;
+                    if (FP8 == FP8_NONE) {
+                        stg16(cache + off, packed);
+                    } else {  // the bf16 key, quantised
+                        float kb[8];
+                        unpack8(packed, kb);
+                        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(cache) + off) =
+                            pack_fp8x8<FP8>(kb, kv_scale[0]);
+                    }
+                }
             }
         }
     }
@@ -212,8 +233,9 @@ extern "C" int dflash_qk_norm_rope_cache_ex(const uint16_t* qkv, int64_t row_str
                                             float eps, const int64_t* positions, const void* cos_sin,
                                             int64_t max_pos, int32_t rotary_dim, int32_t is_neox,
                                             int32_t table_bf16, const int64_t* slots, uint16_t* kv_cache,
-                                            int64_t num_blocks, int32_t block_size, uint16_t* q_out,
-                                            uint16_t* k_out, void* stream) {
+                                            int64_t num_blocks, int32_t block_size, int32_t cache_fp8,
+                                            const float* kv_scale, uint16_t* q_out, uint16_t* k_out,
+                                            void* stream) {
     const void* req[] = {qkv, q_w, k_w, positions, cos_sin, q_out};
     for (const void* q : req)
         if (!q || !DFLASH_ALIGNED16(q)) return DFLASH_ERR_INVALID_ARG;
@@ -225,22 +247,32 @@ extern "C" int dflash_qk_norm_rope_cache_ex(const uint16_t* qkv, int64_t row_str
     if (T_q < 1 || Hq < 1 || Hkv < 1 || max_pos < 1 || !(eps >= 0.f)) return DFLASH_ERR_INVALID_ARG;
     if ((table_bf16 != 0 && table_bf16 != 1) || (is_neox != 0 && is_neox != 1)) return DFLASH_ERR_INVALID_ARG;
     if (rotary_dim < 2 || rotary_dim > D || (rotary_dim & 1)) return DFLASH_ERR_INVALID_ARG;
+    if (cache_fp8 < FP8_NONE || cache_fp8 > FP8_E5M2) return DFLASH_ERR_INVALID_ARG;
+    if (cache_fp8 != FP8_NONE && (!kv_cache || !kv_scale || (reinterpret_cast<uintptr_t>(kv_scale) & 3u)))
+        return DFLASH_ERR_INVALID_ARG;
     if (D != QK_D) return DFLASH_ERR_UNSUPPORTED;
     if (rotary_dim % (is_neox ? 16 : 8) != 0) return DFLASH_ERR_UNSUPPORTED;
     if (row_stride < (int64_t)(Hq + 2 * Hkv) * D || row_stride % 8 != 0) return DFLASH_ERR_INVALID_ARG;
     if (T_q > INT32_MAX || (int64_t)Hq + 2 * (int64_t)Hkv > 65536) return DFLASH_ERR_UNSUPPORTED;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-#define QK_LAUNCH(NX, TB)                                                                                        \
-    hipLaunchKernelGGL((qk_norm_rope_cache_kernel<NX, TB>), dim3((unsigned)T_q), dim3(256), 0, st, qkv, row_stride, \
-                       Hq, Hkv, q_w, k_w, eps, positions, cos_sin, (int)rotary_dim, max_pos, slots, kv_cache,     \
-                       num_blocks, block_size, q_out, k_out)
+#define QK_LAUNCH(NX, TB, F8)                                                                                     \
+    hipLaunchKernelGGL((qk_norm_rope_cache_kernel<NX, TB, F8>), dim3((unsigned)T_q), dim3(256), 0, st, qkv,          \
+                       row_stride, Hq, Hkv, q_w, k_w, eps, positions, cos_sin, (int)rotary_dim, max_pos, slots,       \
+                       kv_cache, num_blocks, block_size, q_out, k_out, kv_scale)
+#define QK_LAUNCH_F8(NX, TB)                                \
+    do {                                                    \
+        if (cache_fp8 == FP8_E4M3) QK_LAUNCH(NX, TB, FP8_E4M3); \
+        else if (cache_fp8 == FP8_E5M2) QK_LAUNCH(NX, TB, FP8_E5M2); \
+        else QK_LAUNCH(NX, TB, FP8_NONE);                   \
+    } while (0)
     if (is_neox) {
-        if (table_bf16) QK_LAUNCH(true, true);
-        else QK_LAUNCH(true, false);
+        if (table_bf16) QK_LAUNCH_F8(true, true);
+        else QK_LAUNCH_F8(true, false);
     } else {
-        if (table_bf16) QK_LAUNCH(false, true);
-        else QK_LAUNCH(false, false);
+        if (table_bf16) QK_LAUNCH_F8(false, true);
+        else QK_LAUNCH_F8(false, false);
     }
+#undef QK_LAUNCH_F8
 #undef QK_LAUNCH
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
@@ -253,6 +285,6 @@ extern "C" int dflash_qk_norm_rope_cache(const uint16_t* qkv, int64_t row_stride
                                          int64_t num_blocks, int32_t block_size, uint16_t* q_out,
                                          uint16_t* k_out, void* stream) {
     return dflash_qk_norm_rope_cache_ex(qkv, row_stride, T_q, Hq, Hkv, D, q_w, k_w, eps, positions, cos_sin,
-                                        max_pos, D, 1, 0, slots, kv_cache, num_blocks, block_size, q_out, k_out,
-                                        stream);
+                                        max_pos, D, 1, 0, slots, kv_cache, num_blocks, block_size, FP8_NONE, nullptr,
+                                        q_out, k_out, stream);
 }

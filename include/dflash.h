@@ -285,9 +285,22 @@ int dflash_linear(const uint16_t* X, const uint16_t* W, int64_t M, int64_t N, in
  *   cos_sin     [max_pos, rotary_dim]: cos of angle index i at column i, sin at
  *               rotary_dim/2 + i; fp32 (table_bf16 = 0, dflash_rope_cos_sin) or
  *               bf16 (table_bf16 = 1, dflash_rope_cos_sin_bf16)
+ *   cache_fp8   the cache's dtype: 0 bf16 (as the plain calls), 1 fp8 E4M3
+ *               ("fn": bias 7, max 448, no infinities), 2 fp8 E5M2 (bias 15,
+ *               max 57344).  With fp8 the cache holds one byte per element
+ *               ([num_blocks, Hkv, block_size, 2D] bytes) and a stored value is
+ *               the bf16 value the bf16 cache would hold (K after its norm and
+ *               RoPE, rounded; V as given or as the linear's bf16 output),
+ *               divided by the layer's scale in fp32, rounded to the nearest
+ *               fp8 value (ties to the even code) and saturated at the largest
+ *               finite one; NaN -> 0x7F.
+ *   kv_scale(s) DEVICE fp32: dflash_qk_norm_rope_cache_ex [2] = {k_scale,
+ *               v_scale}; dflash_context_kv_ex [L, 2], layer l's pair at 2l.
+ *               NULL when cache_fp8 = 0.
  * Requirements: 2 <= rotary_dim <= D, even (else INVALID_ARG); rotary_dim a
  * multiple of 16 with is_neox = 1 and of 8 with is_neox = 0 (else UNSUPPORTED);
- * is_neox, table_bf16 in {0, 1}.  Everything else as in the plain calls.
+ * is_neox, table_bf16 in {0, 1}; cache_fp8 in {0, 1, 2}, and with fp8 a cache
+ * and the scales (else INVALID_ARG).  Everything else as in the plain calls.
  * ---------------------------------------------------------------------- */
 int dflash_qk_norm_rope_cache_ex(const uint16_t* qkv, int64_t row_stride,
                                  int64_t T_q, int32_t Hq, int32_t Hkv, int32_t D,
@@ -296,6 +309,7 @@ int dflash_qk_norm_rope_cache_ex(const uint16_t* qkv, int64_t row_stride,
                                  int32_t rotary_dim, int32_t is_neox, int32_t table_bf16,
                                  const int64_t* slots, uint16_t* kv_cache,
                                  int64_t num_blocks, int32_t block_size,
+                                 int32_t cache_fp8, const float* kv_scale,
                                  uint16_t* q_out, uint16_t* k_out, void* stream);
 int dflash_context_kv_ex(const uint16_t* ctx_states, const uint16_t* hidden_norm_w, float hidden_eps,
                          const uint16_t* W_kv, int64_t num_ctx, int64_t Hd,
@@ -305,6 +319,7 @@ int dflash_context_kv_ex(const uint16_t* ctx_states, const uint16_t* hidden_norm
                          int32_t rotary_dim, int32_t is_neox, int32_t table_bf16,
                          const int64_t* slots, uint16_t* const* caches,
                          int64_t num_blocks, int32_t block_size,
+                         int32_t cache_fp8, const float* kv_scales,
                          uint16_t* kv_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

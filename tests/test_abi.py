@@ -208,9 +208,9 @@ def test_linear_host_validation(L):
 def test_rope_options_host_validation(L):
     f = L.dflash_qk_norm_rope_cache_ex
 
-    def call(rot=128, neox=1, tb=0):
+    def call(rot=128, neox=1, tb=0, f8=0, sc=None):
         return f(FAKE, 24 * 128, 288, 16, 4, 128, FAKE, FAKE, 1e-6, FAKE, FAKE, 4096, rot, neox, tb, FAKE, FAKE,
-                 256, 16, FAKE, None, None)
+                 256, 16, f8, sc, FAKE, None, None)
 
     assert call(rot=127) == 1        # odd
     assert call(rot=0) == 1
@@ -219,15 +219,20 @@ def test_rope_options_host_validation(L):
     assert call(neox=3) == 1
     assert call(rot=24) == 2         # NeoX needs a multiple of 16
     assert call(rot=20, neox=0) == 2  # GPT-J needs a multiple of 8
+    assert call(f8=3) == 1           # cache dtype code
+    assert call(f8=1) == 1           # fp8 without scales
+    assert call(f8=2, sc=FAKE + 2) == 1  # misaligned scales
     g = L.dflash_context_kv_ex
     caches = (ctypes.c_void_p * 2)(FAKE, FAKE)
     ws = L.dflash_context_kv_workspace_size(300, 328)
 
-    def callc(rot=128, neox=1, tb=0):
+    def callc(rot=128, neox=1, tb=0, f8=0, sc=None):
         return g(FAKE, FAKE, 1e-6, FAKE, 300, 328, 2, 2, 128, FAKE, 1e-6, FAKE, FAKE, 4096, rot, neox, tb, FAKE,
-                 ctypes.cast(caches, ctypes.c_void_p), 64, 16, None, FAKE, ws, None)
+                 ctypes.cast(caches, ctypes.c_void_p), 64, 16, f8, sc, None, FAKE, ws, None)
 
     assert callc(rot=130) == 1
     assert callc(tb=-1) == 1
     assert callc(rot=40) == 2
+    assert callc(f8=-1) == 1
+    assert callc(f8=1) == 1          # fp8 without scales
     assert L.dflash_rope_cos_sin_bf16(None, 10, 64, 1e6, None) == 1

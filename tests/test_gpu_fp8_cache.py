@@ -1,0 +1,89 @@
+"""GPU parity of the fp8 K/V cache paths (E4M3fn / E5M2 with per-layer
+scales): the draft layer's fused q/k write and the context K/V precompute store
+the bf16 values their bf16 caches would hold, divided by the scale and rounded
+to fp8; the codes must match the oracle's bit for bit on the same bf16 values."""
+import numpy as np
+import pytest
+
+from oracle import dflash_oracle as O
+import workloads as WL
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x7F  # a NaN code in both formats: never written for finite values
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_draft_candidate_amd as B
+    B.lib()
+    return B
+
+
+@pytest.mark.parametrize("fmt,ks,vs", [("e4m3", 0.05, 0.02), ("e5m2", 0.5, 0.25), ("e4m3", 1.0, 1.0)])
+def test_qk_fp8_cache_write(B, fmt, ks, vs):
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16
+    d = WL.qk_inputs("mid", pad_fraction=0.1)
+    D, Hq, Hkv = d["head_dim"], d["hq"], d["hkv"]
+    cs = B.rope_cos_sin(d["max_pos"], D, d["theta"], "cuda")
+    shape = (d["num_blocks"], Hkv, d["block_size"], 2 * D)
+    cache = torch.full(shape, SENT, dtype=torch.uint8, device="cuda")
+    sc = torch.tensor([ks, vs], dtype=torch.float32, device="cuda")
+    q, k = B.qk_norm_rope_cache(dev_bf16(d["qkv"]), Hq, Hkv, D, dev_bf16(d["q_w"]), dev_bf16(d["k_w"]), d["eps"],
+                                dev(d["positions"]), cs, dev(d["slots"]), cache, cache_fp8=fmt, kv_scale=sc)
+    torch.cuda.synchronize()
+    gk, gc = host_bf16(k), cache.cpu().numpy()
+    v_in = d["qkv"].reshape(-1, Hq + 2 * Hkv, D)[:, Hq + Hkv:]
+    want = np.full(shape, SENT, np.uint8)
+    for t, s in enumerate(d["slots"]):
+        if s < 0:
+            continue
+        b, o = divmod(int(s), d["block_size"])
+        want[b, :, o, :D] = O.bf16_to_fp8_scaled(gk[t], ks, fmt)
+        want[b, :, o, D:] = O.bf16_to_fp8_scaled(v_in[t], vs, fmt)
+    assert np.array_equal(gc, want), f"{fmt}: {int((gc != want).sum())} codes differ"
+    # and the oracle's own path, within its k_out rounding differences
+    rq, rk, rc = O.qk_norm_rope_cache(d["qkv"], Hq, Hkv, D, d["q_w"], d["k_w"], d["eps"], d["positions"],
+                                      d["theta"], d["slots"], np.full(shape, SENT, np.uint8), d["block_size"],
+                                      cache_fp8=fmt, k_scale=ks, v_scale=vs)
+    assert_close(O.bf16_to_f64(gk), O.bf16_to_f64(rk), fmt + " k_out")
+    same_k = np.zeros(shape[:3], bool)
+    for t, s in enumerate(d["slots"]):
+        if s >= 0 and np.array_equal(gk[t], rk[t]):
+            b, o = divmod(int(s), d["block_size"])
+            same_k[b, :, o] = True
+    assert np.array_equal(gc[same_k], rc[same_k])
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_context_kv_fp8_store(B, fmt):
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16
+    d = WL.context_kv_inputs("ctx_small", pad_fraction=0.1)
+    L, D, Hkv = d["layers"], d["head_dim"], d["hkv"]
+    cs = B.rope_cos_sin(d["max_pos"], D, d["theta"], "cuda")
+    shape = (d["num_blocks"], Hkv, d["block_size"], 2 * D)
+    scales = np.array([[0.04, 0.01], [0.5, 2.0]], np.float32)[:L]
+    args = (dev_bf16(d["ctx_states"]), dev_bf16(d["hidden_norm_w"]), d["eps"], dev_bf16(d["W_kv"]), L, Hkv, D,
+            dev_bf16(d["k_norm_w"]), d["eps"], dev(d["positions"]), cs, dev(d["slots"]))
+    c16 = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    kv = B.context_kv(*args, c16, want_kv=True)
+    c8 = [torch.full(shape, SENT, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    B.context_kv(*args, c8, cache_fp8=fmt, kv_scales=torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    kvh = host_bf16(kv)
+    for l in range(L):
+        g16, g8 = host_bf16(c16[l]), c8[l].cpu().numpy()
+        want = np.full(shape, SENT, np.uint8)
+        for t, s in enumerate(d["slots"]):
+            if s < 0:
+                continue
+            b, o = divmod(int(s), d["block_size"])
+            want[b, :, o, :D] = O.bf16_to_fp8_scaled(g16[b, :, o, :D], scales[l, 0], fmt)
+            want[b, :, o, D:] = O.bf16_to_fp8_scaled(kvh[t, l, 1], scales[l, 1], fmt)
+        assert np.array_equal(g8, want), f"{fmt} layer {l}: {int((g8 != want).sum())} codes differ"
