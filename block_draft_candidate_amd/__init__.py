@@ -55,6 +55,9 @@ _SIGS = {
                                          _c_p, _c_p, _c_sz, _c_p]),
     "dflash_block_attn": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i64, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_sz, _c_p]),
+    "dflash_block_attn_ex": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i64, _c_i32, _c_i32,
+                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_p, _c_p,
+                                            _c_sz, _c_p]),
 }
 
 _LIB = None
@@ -288,9 +291,12 @@ def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, pos
 
 # ---------------------------------------------------------------- block attention
 def block_attn(q, kv_cache, block_tables, seq_lens, Lq: int, window: int, scale: float | None = None,
-               out=None, workspace=None, stream=None) -> torch.Tensor:
+               out=None, workspace=None, stream=None, cache_fp8: str | None = None,
+               kv_scale=None) -> torch.Tensor:
     """Non-causal sliding-window attention of each request's ``Lq`` queries
-    ``q [Rq*Lq, Hq, D]`` over the paged cache ``[num_blocks, Hkv, bs, 2D]``."""
+    ``q [Rq*Lq, Hq, D]`` over the paged cache ``[num_blocks, Hkv, bs, 2D]``
+    (bf16, or uint8 fp8 codes with ``cache_fp8`` and the device ``kv_scale``
+    [k_scale, v_scale])."""
     TQ, Hq, D = q.shape
     nblk, Hkv, bs, D2 = kv_cache.shape
     if D2 != 2 * D:
@@ -301,12 +307,13 @@ def block_attn(q, kv_cache, block_tables, seq_lens, Lq: int, window: int, scale:
     scale = D ** -0.5 if scale is None else scale
     out = torch.empty_like(q) if out is None else out
     ws = _workspace(int(lib().dflash_block_attn_workspace_size(Rq, Lq, Hq, D)), q.device, workspace)
-    st = lib().dflash_block_attn(
-        _dev(q, torch.bfloat16, "q"), _dev(kv_cache, torch.bfloat16, "kv_cache"), nblk,
+    f8, sc = _cache_args(cache_fp8, kv_scale, 2)
+    st = lib().dflash_block_attn_ex(
+        _dev(q, torch.bfloat16, "q"), _dev(kv_cache, torch.uint8 if f8 else torch.bfloat16, "kv_cache"), nblk,
         _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
-        _dev(seq_lens, torch.int32, "seq_lens"), Rq, Lq, Hq, Hkv, D, bs, int(window), float(scale),
+        _dev(seq_lens, torch.int32, "seq_lens"), Rq, Lq, Hq, Hkv, D, bs, int(window), float(scale), f8, sc,
         _dev(out, torch.bfloat16, "out"), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "dflash_block_attn")
+    _check(st, "dflash_block_attn_ex")
     return out
 
 

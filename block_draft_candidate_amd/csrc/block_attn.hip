@@ -21,7 +21,12 @@
 //     from the row-major V tile through ds_read_b64_tr_b16 (the transposing LDS
 //     read): lane p of a 16-lane group points at V[key(p / 4)][d0 + 4 (p % 4)],
 //     and lane i receives V[key(j)][d0 + i], j = 0..3.
-#include "common.h"
+//   * With an fp8 cache (E4M3fn or E5M2) the LDS-DMA brings the tile's
+//     256-byte fp8 rows into a ring of staging buffers instead, and after the
+//     tile's barrier the workgroup decodes them (exactly) into one bf16 tile in
+//     the layout above; the rest is the bf16 path.  The layer's K scale is
+//     folded into the score scale and its V scale into the output.
+#include "fp8.h"
 
 namespace dflash {
 
@@ -39,24 +44,31 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 __device__ __forceinline__ void at_fence() { asm volatile("" ::: "memory"); }
 
 // One LDS-DMA instruction: 16 bytes per lane from the cache block at `blk`
-// (one kv head's 16 rows, range-checked to that block) at byte offset `off`,
-// landing at lds + 16 * lane.
-__device__ __forceinline__ void at_load_block_rows(const uint16_t* blk, int off, uint16_t* lds) {
+// (one kv head's 16 rows of `row_bytes`, range-checked to that block) at byte
+// offset `off`, landing at lds + 16 * lane.
+__device__ __forceinline__ void at_load_block_rows(const void* blk, int row_bytes, int off, void* lds) {
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, AT_BS * AT_ROW * 2, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, AT_BS * row_bytes, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 
-template <int G>
+template <int G, int F8>
 __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ cache, int64_t num_blocks,
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ seq_lens, int Lq,
-    int Hq, int Hkv, int window, float scale_log2, uint16_t* __restrict__ out) {
-    constexpr int NI = AT_TK / 2 / G;      // LDS-DMA instructions per wave per tile (2 rows each)
+    int Hq, int Hkv, int window, float scale_log2, uint16_t* __restrict__ out, const float* __restrict__ kv_scale) {
+    // LDS-DMA instructions per wave per tile: 2 bf16 rows or 4 fp8 rows each
+    constexpr int NI = F8 == FP8_NONE ? AT_TK / 2 / G : AT_TK / 4 / G;
+    constexpr int RB = F8 == FP8_NONE ? AT_ROW * 2 : AT_ROW;  // bytes per cache row
     static_assert(NI >= 1, "at least one LDS-DMA instruction per wave");
-    // ring of tiles, then the staged block-table entries (one LDS object)
+    // bf16: a ring of AT_NST tiles; fp8: one bf16 tile, then a ring of AT_NST
+    // fp8 tiles (the same bytes); then the staged block-table entries
     __shared__ __attribute__((aligned(1024))) uint16_t smem[AT_NST * AT_TK * AT_ROW + AT_BTCAP * 2];
     int32_t* const btl = reinterpret_cast<int32_t*>(smem + AT_NST * AT_TK * AT_ROW);
+    static_assert(F8 == FP8_NONE || AT_NST * AT_TK * AT_ROW <= (AT_NST * AT_TK * AT_ROW * 2 - AT_TK * AT_ROW * 2),
+                  "fp8 ring and bf16 tile fit the bf16 ring");
+    uint8_t* const ring8 = reinterpret_cast<uint8_t*>(smem + AT_TK * AT_ROW);
+    if (F8 != FP8_NONE) scale_log2 *= kv_scale[0];
 
     const int r = blockIdx.x / Hkv;
     const int hk = blockIdx.x - r * Hkv;
@@ -99,28 +111,37 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
         return b < 0 ? 0 : (b >= num_blocks ? (int)(num_blocks - 1) : b);
     };
 
-    // DMA lane layout: instruction covers tile rows 2q, 2q+1; lane i -> row 2q + i/32,
-    // physical 16-byte chunk i % 32 of the 512-byte row.  Physical chunk pc < 16 holds
-    // K chunk pc ^ (row % 16); pc >= 16 holds V chunk (pc - 16) ^ (2 (row % 8)).
+    // DMA lane layout (bf16): instruction covers tile rows 2q, 2q+1; lane i -> row
+    // 2q + i/32, physical 16-byte chunk i % 32 of the 512-byte row.  Physical
+    // chunk pc < 16 holds K chunk pc ^ (row % 16); pc >= 16 holds V chunk
+    // (pc - 16) ^ (2 (row % 8)).  (fp8: instruction covers rows 4q .. 4q+3, lane
+    // i -> row 4q + i/16, chunk i % 16 of the 256-byte row, unswizzled.)
     // Per-lane byte offsets inside a cache block (tile-independent), and per
     // tile one scalar block base per instruction.
-    const int dr = lane >> 5;
-    const int pc = lane & 31;
     int loff[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-        const int rr = (2 * (wave_s * NI + j) + dr) & 15;  // row within the cache block
-        const int lchunk = pc < 16 ? (pc ^ rr) : (16 + ((pc - 16) ^ (2 * (rr & 7))));
-        loff[j] = (rr * AT_ROW + lchunk * 8) * 2;
+        if (F8 == FP8_NONE) {
+            const int rr = (2 * (wave_s * NI + j) + (lane >> 5)) & 15;  // row within the cache block
+            const int pc = lane & 31;
+            const int lchunk = pc < 16 ? (pc ^ rr) : (16 + ((pc - 16) ^ (2 * (rr & 7))));
+            loff[j] = (rr * AT_ROW + lchunk * 8) * 2;
+        } else {
+            const int rr = (4 * (wave_s * NI + j) + (lane >> 4)) & 15;
+            loff[j] = rr * AT_ROW + (lane & 15) * 16;
+        }
     }
+    constexpr int RPI = F8 == FP8_NONE ? 2 : 4;  // tile rows per DMA instruction
     auto issue = [&](int tile, int st) {
         const int kb = kstart + tile * AT_TK;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int qd = wave_s * NI + j;
-            const int b = __builtin_amdgcn_readfirstlane(block_of(kb / AT_BS + (2 * qd) / AT_BS));
-            at_load_block_rows(cache + ((int64_t)b * Hkv + hk) * AT_BS * AT_ROW, loff[j],
-                               smem + st * AT_TK * AT_ROW + qd * 512);
+            const int b = __builtin_amdgcn_readfirstlane(block_of(kb / AT_BS + (RPI * qd) / AT_BS));
+            const uint8_t* blk = reinterpret_cast<const uint8_t*>(cache) + ((int64_t)b * Hkv + hk) * AT_BS * RB;
+            void* dst = F8 == FP8_NONE ? (void*)(smem + st * AT_TK * AT_ROW + qd * 512)
+                                       : (void*)(ring8 + st * AT_TK * AT_ROW + qd * 1024);
+            at_load_block_rows(blk, RB, loff[j], dst);
         }
     };
 
@@ -141,7 +162,31 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
         __builtin_amdgcn_s_barrier();  // ... and every wave's; the stage of tile - 1 is free
         at_fence();
         if (tile + AT_NST - 1 < ntiles) issue(tile + AT_NST - 1, (tile + AT_NST - 1) % AT_NST);
-        const uint16_t* tb = smem + st * AT_TK * AT_ROW;
+        if (F8 != FP8_NONE) {
+            // decode the fp8 tile into the bf16 tile (16 codes -> two swizzled
+            // 16-byte chunks per step); the bf16 tile's readers of the previous
+            // tile are past the barrier above
+            const uint8_t* src = ring8 + st * AT_TK * AT_ROW;
+            for (int c = tid; c < AT_TK * 16; c += 64 * G) {
+                const int row = c >> 4, u = c & 15;
+                const u32x4 w = *reinterpret_cast<const u32x4*>(src + row * AT_ROW + u * 16);
+                u32x4 h[2];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t word = w[e >> 1] >> (16 * (e & 1));
+                    h[e >> 2][e & 3] = fp8_to_bf16_bits<F8>(word & 0xFFu) | (fp8_to_bf16_bits<F8>((word >> 8) & 0xFFu) << 16);
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int pch = u < 8 ? ((2 * u + hh) ^ (row & 15)) : (16 + ((2 * (u - 8) + hh) ^ (2 * (row & 7))));
+                    *reinterpret_cast<u32x4*>(smem + row * AT_ROW + pch * 8) = h[hh];
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            at_fence();
+        }
+        const uint16_t* tb = F8 == FP8_NONE ? smem + st * AT_TK * AT_ROW : smem;
         const int kb = kstart + tile * AT_TK;
         // every key of the tile is visible to every query of the block (the
         // highest window start is L - window, for the last query), and every
@@ -233,7 +278,7 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
 
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    const float inv = (lsum > 0.f ? 1.0f / lsum : 0.f) * (F8 == FP8_NONE ? 1.f : kv_scale[1]);
     if (qi < Lq) {
         uint16_t* dst = out + (((int64_t)r * Lq + qi) * Hq + hq) * AT_D;
 #pragma unroll
@@ -249,10 +294,18 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
 template <int G>
 static void launch_attn(const uint16_t* q, const uint16_t* cache, int64_t nblk, const int32_t* bt, int maxb,
                         const int32_t* seq, int64_t Rq, int Lq, int Hq, int Hkv, int window, float scale,
-                        uint16_t* out, hipStream_t st) {
+                        uint16_t* out, int f8, const float* kv_scale, hipStream_t st) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((block_attn_kernel<G>), dim3((unsigned)(Rq * Hkv)), dim3(64 * G), 0, st, q, cache, nblk,
-                       bt, maxb, seq, Lq, Hq, Hkv, window, scale_log2, out);
+    const dim3 grid((unsigned)(Rq * Hkv)), block(64 * G);
+    if (f8 == FP8_E4M3)
+        hipLaunchKernelGGL((block_attn_kernel<G, FP8_E4M3>), grid, block, 0, st, q, cache, nblk, bt, maxb, seq, Lq,
+                           Hq, Hkv, window, scale_log2, out, kv_scale);
+    else if (f8 == FP8_E5M2)
+        hipLaunchKernelGGL((block_attn_kernel<G, FP8_E5M2>), grid, block, 0, st, q, cache, nblk, bt, maxb, seq, Lq,
+                           Hq, Hkv, window, scale_log2, out, kv_scale);
+    else
+        hipLaunchKernelGGL((block_attn_kernel<G, FP8_NONE>), grid, block, 0, st, q, cache, nblk, bt, maxb, seq, Lq,
+                           Hq, Hkv, window, scale_log2, out, kv_scale);
 }
 
 }  // namespace dflash
@@ -264,11 +317,11 @@ extern "C" size_t dflash_block_attn_workspace_size(int64_t Rq, int32_t Lq, int32
     return 0;
 }
 
-extern "C" int dflash_block_attn(const uint16_t* q, const uint16_t* kv_cache, int64_t num_blocks,
-                                 const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
-                                 int64_t Rq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
-                                 int32_t window, float scale, uint16_t* out, void* ws, size_t ws_bytes,
-                                 void* stream) {
+extern "C" int dflash_block_attn_ex(const uint16_t* q, const void* kv_cache, int64_t num_blocks,
+                                    const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                                    int64_t Rq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                    int32_t window, float scale, int32_t cache_fp8, const float* kv_scale,
+                                    uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
     (void)ws; (void)ws_bytes;
     const void* req[] = {q, kv_cache, block_tables, seq_lens, out};
     for (const void* p : req)
@@ -277,18 +330,31 @@ extern "C" int dflash_block_attn(const uint16_t* q, const uint16_t* kv_cache, in
         !(scale > 0.f) || !(scale < INFINITY))
         return DFLASH_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return DFLASH_ERR_INVALID_ARG;
+    if (cache_fp8 < FP8_NONE || cache_fp8 > FP8_E5M2) return DFLASH_ERR_INVALID_ARG;
+    if (cache_fp8 != FP8_NONE && (!kv_scale || (reinterpret_cast<uintptr_t>(kv_scale) & 3u)))
+        return DFLASH_ERR_INVALID_ARG;
     if (D != AT_D || block_size != AT_BS || Lq > 16) return DFLASH_ERR_UNSUPPORTED;
     if (Rq * Hkv > INT32_MAX || (int64_t)max_blocks * AT_BS > INT32_MAX || num_blocks > INT32_MAX)
         return DFLASH_ERR_UNSUPPORTED;
     const int G = Hq / Hkv;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const uint16_t* c = reinterpret_cast<const uint16_t*>(kv_cache);
     switch (G) {
-        case 1: launch_attn<1>(q, kv_cache, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, window, scale, out, st); break;
-        case 2: launch_attn<2>(q, kv_cache, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, window, scale, out, st); break;
-        case 4: launch_attn<4>(q, kv_cache, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, window, scale, out, st); break;
-        case 8: launch_attn<8>(q, kv_cache, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, window, scale, out, st); break;
+        case 1: launch_attn<1>(q, c, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, window, scale, out, cache_fp8, kv_scale, st); break;
+        case 2: launch_attn<2>(q, c, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, window, scale, out, cache_fp8, kv_scale, st); break;
+        case 4: launch_attn<4>(q, c, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, window, scale, out, cache_fp8, kv_scale, st); break;
+        case 8: launch_attn<8>(q, c, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, window, scale, out, cache_fp8, kv_scale, st); break;
         default: return DFLASH_ERR_UNSUPPORTED;
     }
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
+}
+
+extern "C" int dflash_block_attn(const uint16_t* q, const uint16_t* kv_cache, int64_t num_blocks,
+                                 const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                                 int64_t Rq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                 int32_t window, float scale, uint16_t* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    return dflash_block_attn_ex(q, kv_cache, num_blocks, block_tables, max_blocks, seq_lens, Rq, Lq, Hq, Hkv, D,
+                                block_size, window, scale, FP8_NONE, nullptr, out, ws, ws_bytes, stream);
 }

@@ -353,6 +353,23 @@ int dflash_block_attn(const uint16_t* q, const uint16_t* kv_cache, int64_t num_b
                       int32_t block_size, int32_t window, float scale,
                       uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * dflash_block_attn over an fp8 cache: the same attention with
+ * cache_fp8 = 1 (E4M3fn) or 2 (E5M2), kv_cache then one byte per element
+ * [num_blocks, Hkv, block_size, 2D], and K[j, g] = code value * kv_scale[0],
+ * V[j, g] = code value * kv_scale[1] (kv_scale a DEVICE fp32 [2]).  The codes
+ * are decoded exactly (every finite fp8 value is a bf16 value); the scales are
+ * applied to the scores and to the output.  cache_fp8 = 0 is dflash_block_attn
+ * (kv_scale unused).  cache_fp8 outside {0, 1, 2}, or fp8 without scales, is
+ * INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+int dflash_block_attn_ex(const uint16_t* q, const void* kv_cache, int64_t num_blocks,
+                         const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* seq_lens,
+                         int64_t Rq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                         int32_t window, float scale, int32_t cache_fp8, const float* kv_scale,
+                         uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

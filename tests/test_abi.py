@@ -236,3 +236,14 @@ def test_rope_options_host_validation(L):
     assert callc(f8=-1) == 1
     assert callc(f8=1) == 1          # fp8 without scales
     assert L.dflash_rope_cos_sin_bf16(None, 10, 64, 1e6, None) == 1
+
+
+def test_attn_fp8_host_validation(L):
+    f = L.dflash_block_attn_ex
+
+    def call(f8=1, sc=FAKE):
+        return f(FAKE, FAKE, 100, FAKE, 10, FAKE, 4, 16, 32, 8, 128, 16, 2048, 0.088, f8, sc, FAKE, None, 0, None)
+
+    assert call(f8=3) == 1
+    assert call(sc=None) == 1
+    assert call(sc=FAKE + 2) == 1

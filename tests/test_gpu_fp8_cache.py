@@ -87,3 +87,80 @@ def test_context_kv_fp8_store(B, fmt):
             want[b, :, o, :D] = O.bf16_to_fp8_scaled(g16[b, :, o, :D], scales[l, 0], fmt)
             want[b, :, o, D:] = O.bf16_to_fp8_scaled(kvh[t, l, 1], scales[l, 1], fmt)
         assert np.array_equal(g8, want), f"{fmt} layer {l}: {int((g8 != want).sum())} codes differ"
+
+
+def _codes(cache, D, ks, vs, fmt):
+    c = np.empty(cache.shape, np.uint8)
+    c[..., :D] = O.bf16_to_fp8_scaled(cache[..., :D], ks, fmt)
+    c[..., D:] = O.bf16_to_fp8_scaled(cache[..., D:], vs, fmt)
+    return c
+
+
+@pytest.mark.parametrize("fmt,ks,vs", [("e4m3", 0.015, 0.01), ("e5m2", 0.5, 0.25)])
+def test_block_attn_fp8_cache(B, fmt, ks, vs):
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16, say
+    a = WL.attention_inputs("attn", requests=8)
+    D = a["head_dim"]
+    codes = _codes(a["cache"], D, ks, vs, fmt)
+    sc = torch.tensor([ks, vs], dtype=torch.float32, device="cuda")
+    o = B.block_attn(dev_bf16(a["q"]), dev(codes), dev(a["block_tables"]), dev(a["seq_lens"]), a["query_len"],
+                     a["window"], cache_fp8=fmt, kv_scale=sc)
+    torch.cuda.synchronize()
+    ref = O.block_attn(a["q"], codes, a["block_tables"], a["seq_lens"], a["query_len"], a["hq"], a["hkv"], D,
+                       a["block_size"], a["window"], D ** -0.5, cache_fp8=fmt, k_scale=ks, v_scale=vs)
+    g, r = O.bf16_to_f64(host_bf16(o)), O.bf16_to_f64(ref)
+    assert_close(g, r, f"fp8 {fmt} attention")
+    rel = np.abs(g - r).max() / np.sqrt(np.mean(r * r))
+    say(f"[attn fp8 {fmt}] max|d|/rms(ref) = {rel:.3g}")
+    assert rel < 0.1
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_block_attn_fp8_equals_bf16_on_the_decoded_cache(B, fmt):
+    # power-of-two scales: code value * scale is a bf16 number and the scale
+    # multiplications are exact, so the fp8 path must give the bf16 path's bits
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16
+    a = WL.attention_inputs("attn", requests=6)
+    D = a["head_dim"]
+    ks, vs = 0.0078125, 0.0625
+    codes = _codes(a["cache"], D, ks, vs, fmt)
+    dec = O.fp8_to_f64(codes, fmt)
+    dec[..., :D] *= ks
+    dec[..., D:] *= vs
+    bf = O.f64_to_bf16(dec)
+    sc = torch.tensor([ks, vs], dtype=torch.float32, device="cuda")
+    args = (dev(a["block_tables"]), dev(a["seq_lens"]), a["query_len"], a["window"])
+    o8 = B.block_attn(dev_bf16(a["q"]), dev(codes), *args, cache_fp8=fmt, kv_scale=sc)
+    o16 = B.block_attn(dev_bf16(a["q"]), dev_bf16(bf), *args)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(o8), host_bf16(o16))
+
+
+def test_draft_layer_with_an_fp8_cache(B):
+    # the draft layer's own block written fp8 by the fused q/k op, then read by
+    # the attention, against the oracle's same pipeline
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16
+    fmt, ks, vs = "e4m3", 0.015, 0.01
+    a = WL.attention_inputs("attn", requests=6)
+    D = a["head_dim"]
+    codes = _codes(a["cache"], D, ks, vs, fmt)
+    cs = B.rope_cos_sin(a["max_pos"], D, a["theta"], "cuda")
+    cache = dev(codes)
+    sc = torch.tensor([ks, vs], dtype=torch.float32, device="cuda")
+    q, _ = B.qk_norm_rope_cache(dev_bf16(a["qkv"]), a["hq"], a["hkv"], D, dev_bf16(a["q_w"]), dev_bf16(a["k_w"]),
+                                a["eps"], dev(a["positions"]), cs, dev(a["slots"]), cache, want_k=False,
+                                cache_fp8=fmt, kv_scale=sc)
+    o = B.block_attn(q, cache, dev(a["block_tables"]), dev(a["seq_lens"]), a["query_len"], a["window"],
+                     cache_fp8=fmt, kv_scale=sc)
+    torch.cuda.synchronize()
+    rq, _, rc = O.qk_norm_rope_cache(a["qkv"], a["hq"], a["hkv"], D, a["q_w"], a["k_w"], a["eps"], a["positions"],
+                                     a["theta"], a["slots"], codes, a["block_size"], cache_fp8=fmt, k_scale=ks,
+                                     v_scale=vs)
+    ro = O.block_attn(rq, rc, a["block_tables"], a["seq_lens"], a["query_len"], a["hq"], a["hkv"], D,
+                      a["block_size"], a["window"], D ** -0.5, cache_fp8=fmt, k_scale=ks, v_scale=vs)
+    g, r = O.bf16_to_f64(host_bf16(o)), O.bf16_to_f64(ro)
+    assert_close(g, r, "draft layer over an fp8 cache")
+    assert np.abs(g - r).max() / np.sqrt(np.mean(r * r)) < 0.1
