@@ -388,6 +388,41 @@ def main():
     lm_tflops = lmf / (kms["lm_topk"] * 1e-3) / 1e12
     lm_gbs = lmb / (kms["lm_topk"] * 1e-3) / 1e9
 
+    # the attention of step 4 over an fp8 (E4M3) copy of the same cache, per-tensor
+    # scales from the cache's maxima; not part of the step
+    attn_fp8 = {}
+    if not args.no_draft_layer:
+        log("block attention over an fp8 cache ...")
+        Dh = attn["head_dim"]
+        cf = cache.float()
+        ks = float(cf[..., :Dh].abs().max()) / 448.0
+        vs = float(cf[..., Dh:].abs().max()) / 448.0
+        del cf
+        # synthetic fp8 codes of the same cache (torch's cast: input plumbing only)
+        cache8 = torch.empty(cache.shape, dtype=torch.uint8, device=dev)
+        cache8[..., :Dh] = (cache[..., :Dh].float() / ks).to(torch.float8_e4m3fn).view(torch.uint8)
+        cache8[..., Dh:] = (cache[..., Dh:].float() / vs).to(torch.float8_e4m3fn).view(torch.uint8)
+        sc8 = torch.tensor([ks, vs], dtype=torch.float32, device=dev)
+        o8 = torch.empty_like(q_out)
+        for _ in range(args.warmup):
+            B.block_attn(q_out, cache8, tables, seq_lens, Lq, attn["window"], out=o8, cache_fp8="e4m3", kv_scale=sc8)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ms = 0.0
+        for _ in range(args.steps):
+            e0.record()
+            B.block_attn(q_out, cache8, tables, seq_lens, Lq, attn["window"], out=o8, cache_fp8="e4m3", kv_scale=sc8)
+            e1.record()
+            torch.cuda.synchronize()
+            a_ms += e0.elapsed_time(e1)
+        a_ms /= args.steps
+        ab8 = (ab - 2 * Rq_a * Lq * Hq * D * 2) // 2 + 2 * Rq_a * Lq * Hq * D * 2  # K/V bytes halved
+        attn_fp8["block_attn_fp8_e4m3"] = {
+            "ms": a_ms, "GB_per_s": ab8 / (a_ms * 1e-3) / 1e9, "hbm_frac": ab8 / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": ab8,
+            "workload": "step 4's attention over an E4M3 copy of its cache (per-tensor scales); not part of the step"}
+        del cache8
+
     # the draft layer's projections around steps 3-4 (qkv_proj before the
     # q/k norm, o_proj after the attention), timed on their own at the
     # attention workload's 2048 query tokens; not part of the step
@@ -521,6 +556,7 @@ def main():
         result["kernels"]["context_kv"] = ctx_kernel
     result["kernels"].update(lin_kernels)
     result["kernels"].update(hbm_kernels)
+    result["kernels"].update(attn_fp8)
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(cand, attn, edges_per_step, args.cpu_sample)

@@ -23,8 +23,9 @@
 //     and lane i receives V[key(j)][d0 + i], j = 0..3.
 //   * With an fp8 cache (E4M3fn or E5M2) the LDS-DMA brings the tile's
 //     256-byte fp8 rows into a ring of staging buffers instead, and after the
-//     tile's barrier the workgroup decodes them (exactly) into one bf16 tile in
-//     the layout above; the rest is the bf16 path.  The layer's K scale is
+//     tile's barrier the workgroup decodes them into one bf16 tile in the layout
+//     above (hardware fp8 -> fp32 conversions, exact, then the top halves);
+//     the rest is the bf16 path.  The layer's K scale is
 //     folded into the score scale and its V scale into the output.
 #include "fp8.h"
 
@@ -50,6 +51,16 @@ __device__ __forceinline__ void at_load_block_rows(const void* blk, int row_byte
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, AT_BS * row_bytes, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+
+// Two fp8 codes (the low or high half of a word) -> two bf16 packed in a word:
+// v_cvt_pk_f32_fp8 / _bf8 give the OCP E4M3 / E5M2 values exactly as fp32, and
+// every finite one is a bf16 number, so the top halves are exact.
+template <int F8, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    const auto f = F8 == FP8_E4M3 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI)
+                                  : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
+    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
 }
 
 template <int G, int F8>
@@ -172,9 +183,9 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
                 const u32x4 w = *reinterpret_cast<const u32x4*>(src + row * AT_ROW + u * 16);
                 u32x4 h[2];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t word = w[e >> 1] >> (16 * (e & 1));
-                    h[e >> 2][e & 3] = fp8_to_bf16_bits<F8>(word & 0xFFu) | (fp8_to_bf16_bits<F8>((word >> 8) & 0xFFu) << 16);
+                for (int j = 0; j < 4; ++j) {
+                    h[j >> 1][2 * (j & 1)] = fp8x2_to_bf16x2<F8, false>(w[j]);
+                    h[j >> 1][2 * (j & 1) + 1] = fp8x2_to_bf16x2<F8, true>(w[j]);
                 }
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {

@@ -1,7 +1,8 @@
 // fp8 K/V cache codes: OCP E4M3 "fn" (bias 7, max 448, S.1111.111 = NaN, no
-// infinities) and E5M2 (bias 15, max 57344, IEEE-like infinities and NaNs),
-// in plain integer arithmetic so that the result does not depend on a
-// conversion instruction's mode bits.
+// infinities) and E5M2 (bias 15, max 57344, IEEE-like infinities and NaNs).
+// The encoder is plain integer arithmetic, so its rounding and saturation do
+// not depend on a conversion instruction's mode bits.  (Decoding uses the
+// hardware conversions, which give these formats' values exactly.)
 #pragma once
 
 #include "common.h"
@@ -38,26 +39,6 @@ __device__ __forceinline__ uint32_t f32_to_fp8(float x) {
     if (ef >= (1 << EB)) return sign | MAXC;
     const uint32_t code = ((uint32_t)ef << MB) | m;
     return sign | (code > MAXC ? MAXC : code);
-}
-
-// fp8 code -> bf16 bits (exact: every finite fp8 value is a bf16 value).
-template <int FMT>
-__device__ __forceinline__ uint32_t fp8_to_bf16_bits(uint32_t c) {
-    constexpr int EB = FMT == FP8_E4M3 ? 4 : 5;
-    constexpr int MB = FMT == FP8_E4M3 ? 3 : 2;
-    constexpr int BIAS = (1 << (EB - 1)) - 1;
-    const uint32_t sign = (c & 0x80u) << 8;
-    const uint32_t e = (c >> MB) & ((1u << EB) - 1u);
-    const uint32_t m = c & ((1u << MB) - 1u);
-    if (e == 0) {
-        if (m == 0) return sign;
-        const int p = 31 - __builtin_clz(m);  // leading bit of the subnormal's mantissa
-        const uint32_t exp = (uint32_t)(p + 1 - BIAS - MB + 127);
-        return sign | (exp << 7) | ((m - (1u << p)) << (7 - p));
-    }
-    if (FMT == FP8_E4M3 && e == 15 && m == 7) return 0x7FC0u;
-    if (FMT == FP8_E5M2 && e == 31) return sign | (m == 0 ? 0x7F80u : 0x7FC0u);
-    return sign | ((e - BIAS + 127) << 7) | (m << (7 - MB));
 }
 
 // Eight fp32 values divided by a scale -> eight fp8 codes, little-endian in
