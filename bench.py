@@ -233,8 +233,8 @@ def main():
                       key="lm_topk_full" if args.two_kernel_edges else "lm_topk_proj_full")
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path would shard across GPUs "
-              "as described in DESIGN.md but no multi-GPU run is part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the LM head would shard by vocabulary "
+              "and the other kernels by request, but no multi-GPU path is implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -5,7 +5,7 @@ extern "C" const char* dflash_status_string(int status) {
     switch (status) {
         case DFLASH_OK: return "ok";
         case DFLASH_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer or size out of range)";
-        case DFLASH_ERR_UNSUPPORTED: return "unsupported size for this build";
+        case DFLASH_ERR_UNSUPPORTED: return "unsupported size (see the call's requirements)";
         case DFLASH_ERR_WORKSPACE: return "workspace smaller than the size query returned";
         case DFLASH_ERR_HIP: return "HIP launch failure";
         default: return "unknown status";

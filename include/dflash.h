@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
     DFLASH_OK = 0,
     DFLASH_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, k > vocab ... */
-    DFLASH_ERR_UNSUPPORTED = 2, /* a size this build does not handle (see each call) */
+    DFLASH_ERR_UNSUPPORTED = 2, /* a size the library does not handle (see each call) */
     DFLASH_ERR_WORKSPACE = 3,   /* ws smaller than the *_workspace_size query */
     DFLASH_ERR_HIP = 4          /* a HIP launch failed */
 } dflash_status;

@@ -89,7 +89,7 @@ def test_edges_host_validation(L):
     assert call(anchor=None) == 1
     assert call(k=0) == 1
     assert call(R=24) == 2          # R % 16
-    assert call(R=512) == 2         # R > 256 in this build
+    assert call(R=512) == 2         # R > 256
     assert call(k=65, V=4096) == 2
     assert call(wsb=ws - 4) == 3
 
