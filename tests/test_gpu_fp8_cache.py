@@ -164,3 +164,66 @@ def test_draft_layer_with_an_fp8_cache(B):
     g, r = O.bf16_to_f64(host_bf16(o)), O.bf16_to_f64(ro)
     assert_close(g, r, "draft layer over an fp8 cache")
     assert np.abs(g - r).max() / np.sqrt(np.mean(r * r)) < 0.1
+
+
+def test_context_kv_fp8_with_rope_options(B):
+    # fp8 store combined with GPT-J pairing, a partial rotary dim and a bf16 table:
+    # the codes are the quantised bf16 cache of the same options
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16
+    d = WL.context_kv_inputs("ctx_small")
+    L, D, Hkv, rot = d["layers"], d["head_dim"], d["hkv"], 48
+    cs = B.rope_cos_sin(d["max_pos"], rot, d["theta"], "cuda", dtype=torch.bfloat16)
+    shape = (d["num_blocks"], Hkv, d["block_size"], 2 * D)
+    scales = torch.tensor([[0.03, 0.02], [0.06, 0.04]], dtype=torch.float32, device="cuda")[:L]
+    args = (dev_bf16(d["ctx_states"]), dev_bf16(d["hidden_norm_w"]), d["eps"], dev_bf16(d["W_kv"]), L, Hkv, D,
+            dev_bf16(d["k_norm_w"]), d["eps"], dev(d["positions"]), cs, dev(d["slots"]))
+    c16 = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    B.context_kv(*args, c16, rotary_dim=rot, is_neox=False)
+    c8 = [torch.full(shape, SENT, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    B.context_kv(*args, c8, rotary_dim=rot, is_neox=False, cache_fp8="e5m2", kv_scales=scales)
+    torch.cuda.synchronize()
+    sc = scales.cpu().numpy()
+    for l in range(L):
+        g16, g8 = host_bf16(c16[l]), c8[l].cpu().numpy()
+        w = np.any(g8 != SENT, axis=-1)
+        assert np.array_equal(w, np.any(g16 != 0, axis=-1))
+        assert np.array_equal(g8[..., :D][w], O.bf16_to_fp8_scaled(g16[..., :D][w], sc[l, 0], "e5m2"))
+        assert np.array_equal(g8[..., D:][w], O.bf16_to_fp8_scaled(g16[..., D:][w], sc[l, 1], "e5m2"))
+
+
+def test_plain_context_kv_and_attention_equal_the_ex_defaults(B):
+    import ctypes
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16
+    d = WL.context_kv_inputs("ctx_small")
+    L, D, Hkv = d["layers"], d["head_dim"], d["hkv"]
+    cs = B.rope_cos_sin(d["max_pos"], D, d["theta"], "cuda")
+    shape = (d["num_blocks"], Hkv, d["block_size"], 2 * D)
+    x, hw, Wkv, kw = dev_bf16(d["ctx_states"]), dev_bf16(d["hidden_norm_w"]), dev_bf16(d["W_kv"]), dev_bf16(d["k_norm_w"])
+    pos, slots = dev(d["positions"]), dev(d["slots"])
+    c1 = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    B.context_kv(x, hw, d["eps"], Wkv, L, Hkv, D, kw, d["eps"], pos, cs, slots, c1)
+    c2 = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    n, Hd = x.shape
+    ws = torch.empty(B.context_kv_workspace_size(n, Hd), dtype=torch.uint8, device="cuda")
+    ptrs = (ctypes.c_void_p * L)(*[c.data_ptr() for c in c2])
+    st = B.lib().dflash_context_kv(x.data_ptr(), hw.data_ptr(), d["eps"], Wkv.data_ptr(), n, Hd, L, Hkv, D, kw.data_ptr(), d["eps"],
+           pos.data_ptr(), cs.data_ptr(), cs.shape[0], slots.data_ptr(), ctypes.cast(ptrs, ctypes.c_void_p),
+           shape[0], shape[2], None, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    for l in range(L):
+        assert np.array_equal(host_bf16(c1[l]), host_bf16(c2[l]))
+    # attention: the plain call against the binding's _ex call
+    a = WL.attention_inputs("attn", requests=3)
+    q, cache = dev_bf16(a["q"]), dev_bf16(a["cache"])
+    tables, seq = dev(a["block_tables"]), dev(a["seq_lens"])
+    o1 = B.block_attn(q, cache, tables, seq, a["query_len"], a["window"])
+    o2 = torch.empty_like(o1)
+    st = B.lib().dflash_block_attn(q.data_ptr(), cache.data_ptr(), cache.shape[0], tables.data_ptr(), tables.shape[1],
+                                   seq.data_ptr(), seq.shape[0], a["query_len"], a["hq"], a["hkv"], D, 16,
+                                   a["window"], D ** -0.5, o2.data_ptr(), None, 0,
+                                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0 and np.array_equal(host_bf16(o1), host_bf16(o2))
