@@ -146,7 +146,6 @@ __global__ __launch_bounds__(GT_THREADS, 1) void ctx_kv_tiles(
 
     // One pass per head of the tile: the head's 128 columns are staged
     // row-major, then thread t finishes row t.
-#pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         gemm_tile_stage<BN>(stage, acc, pass);
         if (my_row < n) {
