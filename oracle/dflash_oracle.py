@@ -39,7 +39,14 @@ speculator ``vllm.v1.worker.gpu.spec_decode.dflash.speculator``):
   one anchor plus N mask tokens per request -> ``block_attn``.
 
 Where the pages leave a step open, the reading taken is stated in the function.
-Parity pins for every function live in ``tests/test_oracle_*.py``.
+Parity pins for every function live in ``tests/test_oracle_*.py``.  Every
+function is pinned there by closed forms, invariants or brute force; the
+following readings are fixed by nothing on the pages (parity unpinned by the
+pages, the same reading taken by the HIP library): the order of the output
+multiplier and the soft cap, the bf16 rounding of the top-k key, the cache
+layout, the window boundary and the query positions of the block attention,
+the angle formula with a partial rotary dim and the GPT-J pairing, and the
+rounding and saturation of the fp8 cache codes.
 """
 from __future__ import annotations
 
