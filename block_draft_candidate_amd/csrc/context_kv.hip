@@ -5,9 +5,10 @@
 // then per layer the K-norm and NeoX RoPE of K and the slot-mapped write of K
 // and V into that layer's paged cache.
 //
-//   * ctx_hidden_norm: one workgroup per context row; the row's sum of squares
-//     is reduced across the workgroup, the normed row is written once as bf16
-//     (the norm's output dtype) into the workspace.
+//   * ctx_hidden_norm: one workgroup per context row, the row held in
+//     registers; the sum of squares is reduced across the workgroup and the
+//     normed row written once as bf16 (the norm's output dtype) into the
+//     workspace.
 //   * ctx_kv_tiles: the stacked linear as a bf16 MFMA GEMM (32x32x16, fp32
 //     accumulate) over 256 x 256 or 256 x 128 output tiles, with the same
 //     operand pipeline as the LM head's tile kernel (64-wide K slices by LDS-DMA
@@ -39,20 +40,41 @@ struct CtxCaches {
 
 // ---------------------------------------------------------------------------
 // hidden_norm: normed[t, :] = bf16(x[t, :] * (mean(x[t, :]^2) + eps)^-1/2 * w)
+// One workgroup per row.  With CPT > 0 a thread holds its (up to CPT) 16-byte
+// chunks of the row in registers between the reduction and the output, all
+// loads issued up front; CPT = 0 is the general loop (rows past 8192).
 // ---------------------------------------------------------------------------
+template <int CPT>
 __global__ __launch_bounds__(256) void ctx_hidden_norm_kernel(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ w, int Hd, float eps,
                                                               uint16_t* __restrict__ out) {
     __shared__ float red[4];
     const int64_t t = blockIdx.x;
     const uint16_t* row = x + t * Hd;
+    uint16_t* orow = out + t * Hd;
     const int nch = Hd >> 3;  // 16-byte chunks
     float ss = 0.f;
-    for (int c = threadIdx.x; c < nch; c += 256) {
-        float v[8];
-        unpack8(ldg16(row + c * 8), v);
+    u32x4 xv[CPT > 0 ? CPT : 1];
+    if (CPT > 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        for (int i = 0; i < CPT; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            xv[i] = c < nch ? ldg16(row + c * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            float v[8];
+            unpack8(xv[i], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        }
+    } else {
+        for (int c = threadIdx.x; c < nch; c += 256) {
+            float v[8];
+            unpack8(ldg16(row + c * 8), v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
@@ -60,16 +82,24 @@ __global__ __launch_bounds__(256) void ctx_hidden_norm_kernel(const uint16_t* __
     __syncthreads();
     ss = red[0] + red[1] + red[2] + red[3];
     const float rinv = 1.0f / sqrtf(ss / (float)Hd + eps);
-    uint16_t* orow = out + t * Hd;
-    for (int c = threadIdx.x; c < nch; c += 256) {
+    auto put = [&](int c, const u32x4 raw) {
         float v[8], wv[8];
-        unpack8(ldg16(row + c * 8), v);
+        unpack8(raw, v);
         unpack8(ldg16(w + c * 8), wv);
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             o[e] = pack_bf16x2(v[2 * e] * rinv * wv[2 * e], v[2 * e + 1] * rinv * wv[2 * e + 1]);
         stg16(orow + c * 8, o);
+    };
+    if (CPT > 0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            if (c < nch) put(c, xv[i]);
+        }
+    } else {
+        for (int c = threadIdx.x; c < nch; c += 256) put(c, ldg16(row + c * 8));
     }
 }
 
@@ -326,8 +356,18 @@ extern "C" int dflash_context_kv_ex(const uint16_t* ctx_states, const uint16_t* 
     const int per = (int)((ntiles + 7) / 8);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     uint16_t* normed = reinterpret_cast<uint16_t*>(ws);
-    hipLaunchKernelGGL(ctx_hidden_norm_kernel, dim3((unsigned)num_ctx), dim3(256), 0, st, ctx_states, hidden_norm_w,
-                       (int)Hd, hidden_eps, normed);
+    {
+        const int nch = (int)(Hd / 8);
+        const dim3 g((unsigned)num_ctx), b(256);
+        if (nch <= 256)
+            hipLaunchKernelGGL(ctx_hidden_norm_kernel<1>, g, b, 0, st, ctx_states, hidden_norm_w, (int)Hd, hidden_eps, normed);
+        else if (nch <= 512)
+            hipLaunchKernelGGL(ctx_hidden_norm_kernel<2>, g, b, 0, st, ctx_states, hidden_norm_w, (int)Hd, hidden_eps, normed);
+        else if (nch <= 1024)
+            hipLaunchKernelGGL(ctx_hidden_norm_kernel<4>, g, b, 0, st, ctx_states, hidden_norm_w, (int)Hd, hidden_eps, normed);
+        else
+            hipLaunchKernelGGL(ctx_hidden_norm_kernel<0>, g, b, 0, st, ctx_states, hidden_norm_w, (int)Hd, hidden_eps, normed);
+    }
     const dim3 grid((unsigned)(8 * per));
 #define CKV_LAUNCH(BNV, TL)                                                                                         \
     hipLaunchKernelGGL((ctx_kv_tiles<BNV, TL>), grid, dim3(GT_THREADS), 0, st, normed, W_kv, (int)num_ctx, (int)Hd, \

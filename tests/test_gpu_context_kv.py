@@ -122,3 +122,18 @@ def test_context_kv_full_workload(B):
     _, caches2 = _run(B, d, want_kv=False)
     for l in range(d["layers"]):
         assert np.array_equal(caches[l], caches2[l]), f"layer {l}: cache differs without kv_out"
+
+
+@pytest.mark.parametrize("Hd", [6144, 8200])
+def test_context_kv_wide_hidden(B, Hd):
+    # hidden sizes past the 2-chunk-per-thread norm path (4 chunks; the general loop)
+    rng = np.random.default_rng(Hd)
+    n, L, Hkv, D = 37, 1, 1, 128
+    d = dict(ctx_states=WL.to_bf16_bits(rng.standard_normal((n, Hd)).astype(np.float32)),
+             hidden_norm_w=WL.to_bf16_bits((1 + 0.1 * rng.standard_normal(Hd)).astype(np.float32)),
+             W_kv=WL.to_bf16_bits((0.02 * rng.standard_normal((L * 2 * Hkv * D, Hd))).astype(np.float32)),
+             k_norm_w=WL.to_bf16_bits((1 + 0.1 * rng.standard_normal((L, D))).astype(np.float32)),
+             positions=rng.integers(0, 5000, n).astype(np.int64), slots=rng.permutation(64 * 16)[:n].astype(np.int64),
+             num_ctx=n, hidden=Hd, layers=L, hkv=Hkv, head_dim=D, block_size=16, num_blocks=64, eps=1e-6,
+             theta=1e6, max_pos=5000)
+    _check(B, d, f"hidden {Hd}")
