@@ -459,18 +459,21 @@ def main():
 
     # the LM-head top-k where it is bandwidth-bound: 256 rows (the mid
     # workload, and the full vocabulary / hidden size with one position per
-    # request); a 512 MiB scrub write between the timed calls (outside the
+    # request) and 16 rows (one request's block); a 512 MiB scrub write between the timed calls (outside the
     # events) keeps the weight out of the 256 MB last-level cache
     hbm_kernels = {}
     if not args.no_hbm_regime:
-        log("LM-head top-k at 256 rows ...")
+        log("LM-head top-k at 256 and 16 rows ...")
         scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         mid = WL.candidate_inputs("mid")
         cases = [("lm_topk_mid", dbf(mid["H"]), dbf(mid["W"]), mid["top_k"], mid["multiplier"], mid["softcap"],
                   "mid workload: 256 rows (32 requests x 8 steps), vocab 32768, hidden 2048, top_k 8, softcap 30"),
                  ("lm_topk_full_vocab_256_rows", H[:256].contiguous(), W, k, cand["multiplier"], cand["softcap"],
                   "256 rows (one position of 256 requests), vocab 151936, hidden 4096, top_k 16, multiplier 0.5, "
-                  "softcap 30")]
+                  "softcap 30"),
+                 ("lm_topk_full_vocab_16_rows", H[:16].contiguous(), W, k, cand["multiplier"], cand["softcap"],
+                  "16 rows (one request's 16 steps), vocab 151936, hidden 4096, top_k 16, multiplier 0.5, "
+                  "softcap 30; 64-row tiles")]
         for name, Hx, Wx, kx, sx, cx, desc in cases:
             Tx, Hdx = Hx.shape
             Vx = Wx.shape[0]

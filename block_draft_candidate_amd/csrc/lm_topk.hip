@@ -8,7 +8,10 @@
 //
 //   * A workgroup (256 threads, 4 waves in 2 x 2, one per SIMD) owns a 256-row
 //     slice of H and a contiguous run of BN-column tiles of W (its "group").
-//     Each wave computes a 128 x BN/2 block of a 256 x BN tile.  The K loop
+//     Each wave computes a 128 x BN/2 block of a 256 x BN tile.  With 64 rows
+//     or fewer the row tile is 64 (32 x BN/2 per wave): the call is then a
+//     skinny, bandwidth-bound product and the smaller tile saves 3/4 of the
+//     MFMA work.  The K loop
 //     streams 64-wide slices of H and W with LDS-DMA into a ring of five LDS
 //     slots, so the W half of a slice is in flight for two slices.
 //   * Epilogue: the tile is staged through LDS in two column halves; thread t
@@ -113,22 +116,23 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
     L[0] = max(L[0], p);
 }
 
-template <int BN, int KCAP, bool TAIL>
+template <int BM, int BN, int KCAP, bool TAIL>
 __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ W, int T, int V, int Hd,
     int nM, int nN, int G, int xmx, float s, float c, float inv_c,
     uint64_t* __restrict__ part, const uint16_t* __restrict__ Wp, int R, float* __restrict__ hp) {
     constexpr int WN = BN / 2;               // columns per wave
     constexpr int NB = WN / 32;              // 32-column MFMA blocks per wave
-    constexpr int MB = 4;                    // 32-row MFMA blocks per wave (128 rows)
-    constexpr int NIA = LM_BM / 8 / 4;       // LDS-DMA instructions per wave per slice (A)
+    constexpr int MB = BM / 64;              // 32-row MFMA blocks per wave (BM / 2 rows)
+    constexpr int NIA = BM / 8 / 4;          // LDS-DMA instructions per wave per slice (A)
     constexpr int NIB = BN / 8 / 4;          // (B)
-    constexpr int UNIT = (LM_BM > BN ? LM_BM : BN) * LM_BK;  // elements of one operand's K slice
+    constexpr int UNIT = (BM > BN ? BM : BN) * LM_BK;  // elements of one operand's K slice
     constexpr int NSLOT = 5;                 // LDS ring of operand slices (2.5 K slices)
     constexpr int QCOLS = WN;                // epilogue pass width: one wave's columns
     constexpr int MW = QCOLS / 32;           // 32-bit words of a pass's candidate mask
     constexpr int SP = QCOLS + 4;            // row pitch (floats) of the epilogue staging
-    constexpr int SMEM = (NSLOT * UNIT > LM_BM * SP * 2) ? NSLOT * UNIT : LM_BM * SP * 2;
+    constexpr int SMEM = (NSLOT * UNIT > BM * SP * 2) ? NSLOT * UNIT : BM * SP * 2;
+    static_assert(BM == 256 || BM == 64, "row tile");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
     float* stage = reinterpret_cast<float*>(smem);
 
@@ -155,9 +159,11 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     }
     const int n_begin = (int)((int64_t)g * nN / G);
     const int n_end = (int)((int64_t)(g + 1) * nN / G);
-    const int m0 = m_tile * LM_BM;
+    const int m0 = m_tile * BM;
     const int gcol0 = n_begin * BN;
     const int my_row = m0 + tid;
+    // thread t owns row t of the tile (rows past BM: none); evaluated where used
+    auto row_ok = [&]() { return (BM >= LM_THREADS || tid < BM) && my_row < T; };
 
     uint32_t list[KCAP];
 #pragma unroll
@@ -166,12 +172,12 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
 
     const int nK = (Hd + LM_BK - 1) / LM_BK;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(H + (int64_t)m0 * Hd), (short)0, min(LM_BM, T - m0) * Hd * 2, 0x00020000);
+        (void*)(H + (int64_t)m0 * Hd), (short)0, min(BM, T - m0) * Hd * 2, 0x00020000);
 
     // Per-lane LDS element offsets of the 32 x 16 fragments: row = lane % 32 of
     // each 32-row block, 16-byte chunk (2 * k16 + lane / 32) ^ swz8(row).
     const int fr = lane & 31;
-    const int a_row0 = (wm * 128 + fr) * LM_BK;
+    const int a_row0 = (wm * (BM / 2) + fr) * LM_BK;
     const int b_row0 = (wn * WN + fr) * LM_BK;
 
     // The rank projection, when hp is given: W_proj's R rows are appended to the
@@ -246,10 +252,12 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
         // and the group barriers then spread both between the MFMAs (reads
         // first, one per MFMA).
         constexpr int MPK = MB * NB;  // MFMAs per K step
+        // fragment reads and DMA loads per K step: every one of each kind
+        constexpr int NQ = NFR > NIA ? (NFR > NIB ? NFR : NIB) : (NIA > NIB ? NIA : NIB);
         auto kstep = [&](const bf16x8 (&fa)[MB], const bf16x8 (&fb)[NB], int ra, int rb, int rk16,
                          bf16x8 (&na)[MB], bf16x8 (&nb)[NB], int dma, int dkt, int dslot) {
 #pragma unroll
-            for (int q = 0; q < (NFR > NIA ? NFR : NIA); ++q) {
+            for (int q = 0; q < NQ; ++q) {
                 if (q < NFR && rk16 >= 0) read_frag(ra, rb, rk16, q, na, nb);
                 if (dma == 1 && q < NIA)
                     dma_one<NIA, TAIL>(rsA, smem + dslot * UNIT, voffA, lcA, wave_s, hd_t, dkt * LM_BK, q);
@@ -258,8 +266,8 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
             }
             mfmas(fa, fb);
 #pragma unroll
-            for (int q = 0; q < MPK; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int q = 0; q < (MPK > NQ ? MPK : NQ); ++q) {
+                if (q < MPK) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (q < NFR && rk16 >= 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 if ((dma == 1 && q < NIA) || (dma == 2 && q < NIB)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                             // to VGPRs and spill.  (lgkmcnt is waited for explicitly
                             // before the barrier below.)
                             const uint32_t dst = lds_offset(
-                                stage + (wm * 128 + i * 32 + 8 * b + 4 * (lane >> 5)) * SP + col);
+                                stage + (wm * (BM / 2) + i * 32 + 8 * b + 4 * (lane >> 5)) * SP + col);
                             asm volatile("ds_write_b32 %0, %1" ::"v"(dst), "a"(acc[i][j][4 * b]) : "memory");
                             asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(dst), "a"(acc[i][j][4 * b + 1]),
                                          "i"(SP * 4) : "memory");
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging writes done
             __builtin_amdgcn_s_barrier();
             compiler_fence();
-            if (my_row < T && proj) {
+            if (row_ok() && proj) {
                 // a projection tile: the row's raw fp32 sums (no scale, cap or
                 // selection) go to hp; columns past R were read as zero
                 const int cbase = n0 + pass * QCOLS;
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                 } else {
                     for (int cc = 0; cc < ncols; ++cc) dstp[cc] = rowp[cc];
                 }
-            } else if (my_row < T) {
+            } else if (row_ok()) {
                 const int cbase = n0 + pass * QCOLS;
                 const int ncols = min(QCOLS, V - cbase);
                 const float* rowp = stage + tid * SP;
@@ -437,7 +445,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                 }
                 if (changed && list[KCAP - 1] != 0u) thr = acc_lower_bound(list[KCAP - 1] >> 16, s, c);
             }
-            if (my_row < T && mixed) {
+            if (row_ok() && mixed) {
                 // the mixed tile's projection columns V .. V + R - 1 (R % 4 == 0,
                 // V % 4 == 0: 16-byte aligned)
                 const int cbase = n0 + pass * QCOLS;
@@ -455,7 +463,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
         }
     }
 
-    if (my_row < T) {
+    if (row_ok()) {
         uint64_t* dst = part + ((int64_t)my_row * G + g) * KCAP;
 #pragma unroll
         for (int j = 0; j < KCAP; ++j) {
@@ -558,7 +566,7 @@ __global__ __launch_bounds__(256) void lm_topk_merge16_level(const uint64_t* __r
 }
 
 struct LmPlan {
-    int BN, KCAP, nM, nN, G, xmx;
+    int BM, BN, KCAP, nM, nN, G, xmx;
     int64_t nwg;
     size_t ws;
 };
@@ -566,7 +574,11 @@ struct LmPlan {
 static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p) {
     (void)Hd;
     p.KCAP = k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
-    p.nM = (int)((T + LM_BM - 1) / LM_BM);
+    // Up to 64 rows the contraction is far from dense: 64-row tiles do a quarter
+    // of a 256-row tile's MFMA work for the same weight stream, and 128-column
+    // tiles spread the vocabulary over more workgroups.
+    p.BM = T <= 64 ? 64 : LM_BM;
+    p.nM = (int)((T + p.BM - 1) / p.BM);
     const int target = 256;  // one workgroup per CU (the tile kernel fills a CU's LDS)
     auto groups = [&](int BN) {
         const int64_t nN = (V + BN - 1) / BN;
@@ -580,7 +592,7 @@ static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p) {
         p.G = (int)G;
     };
     groups(256);
-    if ((int64_t)p.nM * p.G < target) groups(128);
+    if (p.BM == 64 || (int64_t)p.nM * p.G < target) groups(128);
     p.nwg = (int64_t)p.nM * p.G;
     if (p.nwg > (int64_t)1 << 30) return false;
     // XCD blocks: xmx row tiles x (per / xmx) groups per XCD, xmx the divisor of
@@ -612,26 +624,28 @@ struct LmProj {
     float* hp;
 };
 
-template <int BN, int KCAP>
+template <int BM, int BN, int KCAP>
 static void launch_tiles(const LmPlan& p, const uint16_t* H, const uint16_t* W, int T, int V, int Hd,
                          float s, float c, uint64_t* part, const LmProj& pj, hipStream_t st) {
     const float inv_c = c > 0.f ? 1.0f / c : 0.f;
     if (Hd % LM_BK == 0)
-        hipLaunchKernelGGL((lm_topk_tiles<BN, KCAP, false>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H, W,
-                           T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
+        hipLaunchKernelGGL((lm_topk_tiles<BM, BN, KCAP, false>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H,
+                           W, T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
     else
-        hipLaunchKernelGGL((lm_topk_tiles<BN, KCAP, true>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H, W,
-                           T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
+        hipLaunchKernelGGL((lm_topk_tiles<BM, BN, KCAP, true>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H,
+                           W, T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
 }
 
 template <int KCAP>
 static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, int T, int V, int Hd, int k,
                        float s, float c, uint64_t* part, int32_t* ids, float* logits, const LmProj& pj,
                        hipStream_t st) {
-    if (p.BN == 256)
-        launch_tiles<256, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
+    if (p.BM == 64)
+        launch_tiles<64, 128, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
+    else if (p.BN == 256)
+        launch_tiles<LM_BM, 256, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
     else
-        launch_tiles<128, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
+        launch_tiles<LM_BM, 128, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
     const uint64_t* cur = part;
     int G = p.G;
     if (G > 16) {

@@ -102,3 +102,27 @@ def test_large_vocab_tie_heavy_sampled_rows(B):
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 14)]))
     _check(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"], rows, "large")
+
+
+@pytest.fixture(scope="module")
+def full_inputs():
+    from tests.gpu_common import candidate
+    return candidate("full")
+
+
+@pytest.mark.parametrize("T", [16, 33, 64])
+def test_skinny_rows_full_vocab(B, full_inputs, T):
+    """Up to 64 rows the head runs 64-row tiles: every row of the full
+    vocabulary's product against the oracle, 16 / 33 (a ragged tile) / 64."""
+    d = full_inputs
+    H = np.ascontiguousarray(d["H"][(T * 37) % 1000:][:T])
+    _check(B, H, d["W"], d["top_k"], d["multiplier"], d["softcap"], label=f"skinny T{T}")
+
+
+@pytest.mark.parametrize("T,V,Hd,k", [
+    (50, 70001, 1000, 8),    # 64-row tile with a K tail and a ragged vocabulary
+    (64, 300, 64, 64),       # fewer columns than groups: one tile per group, k = 64
+])
+def test_skinny_ragged(B, T, V, Hd, k):
+    H, W = _random_case(T + V + Hd, T, V, Hd, 0.1)
+    _check(B, H, W, k, 0.75, 20.0, label=f"skinny T{T} V{V} Hd{Hd} k{k}")
