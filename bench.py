@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--no-hbm-regime", action="store_true",
                     help="skip the LM-head top-k at 256 rows (mid workload; full vocabulary, one position per "
                          "request), where it is HBM-bound")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the edge call at the tiny / mid / full / large configurations and the LM-head "
+                         "top-k at tiny / large (context lines, not part of the step)")
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="the oracle baseline runs 1/N of the step's requests (default 4: about 10-20 s on 16 cores)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -503,6 +506,112 @@ def main():
                 "workload": desc + " (median of the timed calls, cache scrubbed before each; not part of the step)"}
         del scrub
 
+    # the other configurations, as context: dflash_candidate_edges (projection
+    # inside the call, as the edge metric counts it) at every configuration and
+    # dflash_lm_topk at the two not timed above, each against its binding
+    # roofline; median of the timed calls, a 512 MiB scrub write before each
+    other_kernels = {}
+    if not args.no_other_configs:
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def large_inputs_on_device():
+            """The large configuration drawn on the GPU (seeded torch generator),
+            so that the 1.3 G-element LM head and 8192 rows of 32 distinct ids do
+            not take minutes on the host: the same shapes and distributions as
+            the workload module's draw (N(0,1) hidden states, N(0, 0.02) weights
+            with the LM head rounded to 4 explicit mantissa bits, ids uniform
+            and distinct within a row, unary logits at the logits' scale)."""
+            c = WL.CONFIGS["large"]
+            Rl, Sl, kl, Vl, Hdl, Rkl = c["requests"], c["steps"], c["top_k"], c["vocab"], c["hidden"], c["rank"]
+            g = torch.Generator(device=dev)
+            g.manual_seed(c["seed"])
+            nrm = lambda shape, sg: (torch.randn(shape, generator=g, device=dev) * sg).to(torch.bfloat16)
+            Wl = nrm((Vl, Hdl), WL.SIGMA_W)
+            # RNE of the bf16 bits to 4 explicit mantissa bits (drop 3): the
+            # magnitude bits round as an integer, a carry moves into the exponent
+            b = Wl.view(torch.int16).to(torch.int32) & 0xFFFF
+            b = ((b + 3 + ((b >> 3) & 1)) & 0xFFF8) & 0xFFFF
+            Wl = torch.where(b >= 0x8000, b - 0x10000, b).to(torch.int16).view(torch.bfloat16)
+            Tl = Rl * Sl
+            # id = kl * r + j for a uniform r: distinct residues mod kl, so
+            # distinct within a row (Vl % kl == 0)
+            ids_l = (torch.randint(0, Vl // kl, (Rl, Sl, kl), generator=g, device=dev) * kl
+                     + torch.arange(kl, device=dev)).to(torch.int32)
+            return dict(H=nrm((Tl, Hdl), 1.0), W=Wl, P=nrm((Vl, Rkl), WL.SIGMA_W), S=nrm((Vl, Rkl), WL.SIGMA_W),
+                        Wp=nrm((Rkl, Hdl), WL.SIGMA_W), ids=ids_l,
+                        U=torch.randn((Rl, Sl, kl), generator=g, device=dev) * (WL.SIGMA_W * Hdl ** 0.5),
+                        anchor=torch.randint(0, Vl, (Rl,), generator=g, device=dev).to(torch.int32),
+                        requests=Rl, steps=Sl, top_k=kl, vocab=Vl, hidden=Hdl, rank=Rkl,
+                        softcap=c["softcap"], multiplier=c["multiplier"])
+
+        def on_dev(x, bf=False):
+            if isinstance(x, torch.Tensor):
+                return x
+            return dbf(x) if bf else torch.from_numpy(x).to(dev)
+
+        def median_ms(fn, reps):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            tms = []
+            for _ in range(reps):
+                scrub.fill_(1)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                tms.append(e0.elapsed_time(e1))
+            tms.sort()
+            return tms[len(tms) // 2]
+
+        for name in ("tiny", "mid", "full", "large"):
+            log(f"edges (and LM head) at the {name} configuration ...")
+            d = cand if name == "full" else large_inputs_on_device() if name == "large" else \
+                WL.candidate_inputs(name)
+            Rx, Sx, kx, Vx, Hdx, Rkx = (d["requests"], d["steps"], d["top_k"], d["vocab"], d["hidden"],
+                                        d["rank"])
+            Tx = Rx * Sx
+            Hx = H if name == "full" else on_dev(d["H"], True)
+            Px, Sx_cb, Wpx = (P, Sc, Wp) if name == "full" else (on_dev(d["P"], True), on_dev(d["S"], True),
+                                                                  on_dev(d["Wp"], True))
+            idsx, ux, anx = on_dev(d["ids"]), on_dev(d["U"]), on_dev(d["anchor"])
+            ex = torch.empty((Rx, Sx, kx, kx), dtype=torch.float32, device=dev)
+            wsx = torch.empty(max(16, B.candidate_edges_workspace_size(Tx, Rkx, Hdx)), dtype=torch.uint8,
+                              device=dev)
+            ms = median_ms(lambda: B.candidate_edges(Px, Sx_cb, idsx, ux, Hx, Wpx, anx, ex, wsx), 20)
+            xb = edge_bytes(Rx, Sx, kx, Rkx, Hdx)
+            xf = 2 * Tx * Rkx * Hdx + Tx * (kx * Rkx + 2 * kx * kx * Rkx)
+            floor_ms = max(xb / (HBM_PEAK_GBS * 1e9), xf / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+            other_kernels[f"edges_{name}"] = {
+                "ms": ms, "edge_scores_per_s": Tx * kx * kx / (ms * 1e-3),
+                "GB_per_s": xb / (ms * 1e-3) / 1e9, "hbm_frac": xb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "binding_roofline_frac": floor_ms / ms, "algorithmic_bytes": xb, "flops": xf,
+                "workload": f"dflash_candidate_edges (projection in the call) at the {name} configuration: "
+                            f"{Rx} requests x {Sx} steps, top_k {kx}, vocab {Vx}, rank {Rkx}, hidden {Hdx} "
+                            "(not part of the step)"}
+            if name in ("tiny", "large"):
+                Wx = on_dev(d["W"], True)
+                idl = torch.empty((Tx, kx), dtype=torch.int32, device=dev)
+                lgl = torch.empty((Tx, kx), dtype=torch.float32, device=dev)
+                wsl = torch.empty(max(16, B.lm_topk_workspace_size(Tx, Vx, Hdx, kx)), dtype=torch.uint8,
+                                  device=dev)
+                ms = median_ms(lambda: B.lm_topk(Hx, Wx, kx, d["multiplier"], d["softcap"], idl, lgl, wsl),
+                               9 if name == "large" else 20)
+                xb, xf = lm_bytes(Tx, Vx, Hdx, kx), lm_flops(Tx, Vx, Hdx)
+                floor_ms = max(xb / (HBM_PEAK_GBS * 1e9), xf / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+                other_kernels[f"lm_topk_{name}"] = {
+                    "ms": ms, "GB_per_s": xb / (ms * 1e-3) / 1e9,
+                    "hbm_frac": xb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "TFLOP_per_s": xf / (ms * 1e-3) / 1e12,
+                    "mfma_frac": xf / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "binding_roofline_frac": floor_ms / ms, "algorithmic_bytes": xb, "flops": xf,
+                    "workload": f"dflash_lm_topk at the {name} configuration: {Tx} rows, vocab {Vx}, hidden "
+                                f"{Hdx}, top_k {kx}, multiplier {d['multiplier']}, softcap {d['softcap']} "
+                                "(not part of the step)"}
+                del Wx
+            del d
+        del scrub
+
     result = {
         "metric": METRIC,
         "value": value,
@@ -560,6 +669,7 @@ def main():
     result["kernels"].update(lin_kernels)
     result["kernels"].update(hbm_kernels)
     result["kernels"].update(attn_fp8)
+    result["kernels"].update(other_kernels)
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(cand, attn, edges_per_step, args.cpu_sample)
