@@ -58,6 +58,21 @@ def test_large_workload_subset(B):
     check_edges(E, _ref(d), d["U"], "large")
 
 
+def test_large_full_size_sampled_requests(B):
+    """The large configuration at its full 512 x 16 rows, the launch the
+    benchmark times (two K slices of the projection, the k = 32 / rank 256
+    bilinear tile); the oracle checks whole requests spread over the batch."""
+    d = WL.candidate_inputs("large")
+    Rq, S = d["requests"], d["steps"]
+    E = _gpu_edges(B, d)
+    assert E.shape == d["ids"].shape + (d["top_k"],)
+    g = np.random.default_rng(17)
+    req = np.unique(np.concatenate([[0, 1, Rq - 1], g.integers(0, Rq, 9)]))
+    rows = (req[:, None] * S + np.arange(S)).reshape(-1)
+    ref = O.candidate_edges(d["P"], d["S"], d["ids"][req], d["U"][req], d["H"][rows], d["Wp"], d["anchor"][req])
+    check_edges(E[req], ref, d["U"][req], "large, full size")
+
+
 @pytest.mark.parametrize("Rq,S,k,V,R,Hd", [
     (3, 5, 3, 100, 16, 24),       # k < 16, R = 16 (4-wide lane chunks), Hd % 64 != 0
     (5, 2, 20, 300, 48, 520),     # k in (16, 32], R % 32 != 0

@@ -144,13 +144,23 @@ def keep_mantissa_bits(bits: np.ndarray, m: int) -> np.ndarray:
     drop = 7 - m
     if drop <= 0:
         return bits
-    u = bits.astype(np.uint32)
+    flat = np.ascontiguousarray(bits).reshape(-1)
+    out = np.empty_like(flat)
     half = np.uint32(1 << (drop - 1))
-    lsb = (u >> np.uint32(drop)) & np.uint32(1)
-    r = ((u + half - np.uint32(1) + lsb) >> np.uint32(drop)) << np.uint32(drop)
-    keep_special = (u & np.uint32(0x7F80)) == np.uint32(0x7F80)  # inf / nan untouched
-    r = np.where(keep_special, u, r)
-    return (r & np.uint32(0xFFFF)).astype(np.uint16)
+
+    def part(lo: int) -> None:
+        # in chunks: full-size uint32 temporaries of a 1.3 G-element weight
+        # take minutes to page in
+        u = flat[lo:lo + _CHUNK].astype(np.uint32)
+        lsb = (u >> np.uint32(drop)) & np.uint32(1)
+        r = ((u + half - np.uint32(1) + lsb) >> np.uint32(drop)) << np.uint32(drop)
+        keep_special = (u & np.uint32(0x7F80)) == np.uint32(0x7F80)  # inf / nan untouched
+        r = np.where(keep_special, u, r)
+        out[lo:lo + _CHUNK] = (r & np.uint32(0xFFFF)).astype(np.uint16)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(part, range(0, flat.size, _CHUNK)))
+    return out.reshape(np.shape(bits))
 
 
 # --------------------------------------------------------------------------
