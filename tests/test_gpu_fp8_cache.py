@@ -227,3 +227,34 @@ def test_plain_context_kv_and_attention_equal_the_ex_defaults(B):
                                    torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0 and np.array_equal(host_bf16(o1), host_bf16(o2))
+
+
+def test_block_attn_fp8_full_size_equals_bf16_on_the_decoded_cache(B):
+    """The attention workload at its full 128 requests over an E4M3 cache (the
+    launch the benchmark times): with power-of-two scales the fp8 path must
+    give the bf16 path's bits on the decoded cache, and the bf16 path is
+    checked against the oracle at this size elsewhere.  Codes and decoded
+    values come from torch's own fp8 casts, not from this library."""
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16
+    a = WL.attention_inputs("attn")
+    D = a["head_dim"]
+    ks, vs = 0.03125, 0.03125  # |K| <= sqrt(128) and |V| < 14 stay below 448 * scale
+    c = dev_bf16(a["cache"]).float()
+    c[..., :D] /= ks
+    c[..., D:] /= vs
+    codes = c.to(torch.float8_e4m3fn)
+    dec = codes.float()
+    assert not torch.isnan(dec).any()  # no value past the format's range
+    dec[..., :D] *= ks
+    dec[..., D:] *= vs
+    bf = dec.to(torch.bfloat16)
+    assert torch.equal(bf.float(), dec)  # the decoded values are bf16 numbers
+    del c, dec
+    sc = torch.tensor([ks, vs], dtype=torch.float32, device="cuda")
+    args = (dev(a["block_tables"]), dev(a["seq_lens"]), a["query_len"], a["window"])
+    q = dev_bf16(a["q"])
+    o8 = B.block_attn(q, codes.view(torch.uint8), *args, cache_fp8="e4m3", kv_scale=sc)
+    o16 = B.block_attn(q, bf, *args)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(o8), host_bf16(o16))

@@ -97,10 +97,13 @@ def test_full_workload_sampled_rows(B):
 
 
 def test_large_vocab_tie_heavy_sampled_rows(B):
-    d = WL.candidate_inputs("large", requests=64)
+    """The large configuration at its full 8192 rows (the launch the benchmark
+    times): 32 row tiles, k = 32, a tie-heavy LM head; rows from every fourth
+    row tile."""
+    d = WL.candidate_inputs("large")
     T = d["H"].shape[0]
     rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 14)]))
+    rows = np.unique(np.concatenate([[0, 255, 256, T - 1], np.arange(0, T, 1024) + rng.integers(0, 1024, T // 1024)]))
     _check(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"], rows, "large")
 
 
@@ -126,3 +129,13 @@ def test_skinny_rows_full_vocab(B, full_inputs, T):
 def test_skinny_ragged(B, T, V, Hd, k):
     H, W = _random_case(T + V + Hd, T, V, Hd, 0.1)
     _check(B, H, W, k, 0.75, 20.0, label=f"skinny T{T} V{V} Hd{Hd} k{k}")
+
+
+def test_256_rows_full_vocab(B, full_inputs):
+    """256 rows over the full vocabulary (one row tile, 256 groups of 256
+    columns, two merge levels): the benchmark's bandwidth-regime launch."""
+    d = full_inputs
+    H = np.ascontiguousarray(d["H"][:256])
+    rng = np.random.default_rng(256)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255], rng.integers(0, 256, 19)]))
+    _check(B, H, d["W"], d["top_k"], d["multiplier"], d["softcap"], rows, "256 rows full vocab")
