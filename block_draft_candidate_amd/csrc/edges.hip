@@ -11,9 +11,10 @@
 //      LDS-DMA ring keeps enough bytes in flight per CU.
 //   2. edges_bilinear: one wave per (request, step), independent of the other
 //      waves of its workgroup.  It issues all of its loads up front (ids, h_p
-//      partials, unary logits), then moves its 16 * KB predecessor and candidate
-//      codebook rows straight into LDS (global_load_lds, 16 bytes per lane), so
-//      the wave waits on two memory latencies only: the ids, then the rows they
+//      partials, unary logits), then loads its 16 * KB candidate (successor)
+//      codebook rows straight into registers in the MFMA B layout and moves its
+//      predecessor rows into LDS (global_load_lds, 16 bytes per lane), so the
+//      wave waits on two memory latencies only: the ids, then the rows they
 //      name.  a = P[pred] * h_p is formed in fp32 and split into three bf16 parts
 //      whose products with the bf16 successor rows are exact, so the k x k block
 //      comes out of bf16 MFMA with fp32 products and fp32 accumulation.
@@ -127,10 +128,10 @@ __global__ __launch_bounds__(PJ_THREADS) void edges_projection(const uint16_t* _
         }
 }
 
-// Per-wave LDS tile: NR = 16 * KB gathered rows of each codebook, packed at 2R
-// bytes, NJ LDS-DMA instructions of 1 KB (the last one padded), then the KS
+// Per-wave LDS tile: NR = 16 * KB gathered predecessor-codebook rows, packed at
+// 2R bytes, NJ LDS-DMA instructions of 1 KB (the last one padded), then the KS
 // projection partials of the wave's row (fp32 [KS, R], NH instructions) and its
-// unary logits (fp32 [k <= 64]).
+// unary logits (fp32 [k <= 64]).  The successor rows go straight to registers.
 template <int KB, int R, int KS>
 struct EdgeTile {
     static constexpr int NR = 16 * KB;
@@ -138,7 +139,7 @@ struct EdgeTile {
     static constexpr int NJ = (NR * CPR + 63) / 64;
     static constexpr int TILE = NJ * 512;                  // elements per codebook
     static constexpr int NH = (KS * R / 4 + 63) / 64;      // LDS-DMA instructions for the partials
-    static constexpr int WAVE_ELEMS = 2 * TILE + NH * 512 + 128;   // + 64 fp32 unary logits
+    static constexpr int WAVE_ELEMS = TILE + NH * 512 + 128;   // + 64 fp32 unary logits
     static constexpr int WAVE_BYTES = WAVE_ELEMS * 2;
 };
 
@@ -198,8 +199,7 @@ __global__ __launch_bounds__(64 * WAVES) void edges_bilinear(
     const int r = tt / St, p = tt - r * St;
     const int g = lane >> 4, li = lane & 15;
     uint16_t* sP = smem_e + wave_s * TL::WAVE_ELEMS;
-    uint16_t* sS = sP + TL::TILE;
-    float* sH = reinterpret_cast<float*>(sS + TL::TILE);
+    float* sH = reinterpret_cast<float*>(sP + TL::TILE);
     float* sU = sH + TL::NH * 256;
 
     // ids of the predecessor rows (q) and candidate rows (c) this lane stands for;
@@ -219,26 +219,36 @@ __global__ __launch_bounds__(64 * WAVES) void edges_bilinear(
         cid[b] = in ? min(max(cid[b], 0), V - 1) : 0;
     }
 
-    // gathers; chunks past the tile (f >= NR * CPR) reload row 0 into the padding
+    // the successor rows, in the MFMA B layout: lane (g, li) holds ranks
+    // 32 ic + 8 g .. + 7 of candidate row 16 b + li (and ranks 32 NC + 4 g .. + 3
+    // of a last 16-rank chunk), which is its own cid[b]
+    u32x4 sv[KB][NC > 0 ? NC : 1];
+    u32x2 sh[KB];
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+        const uint16_t* srow = Sc + (int64_t)cid[b] * R;
+#pragma unroll
+        for (int ic = 0; ic < NC; ++ic) sv[b][ic] = *reinterpret_cast<const u32x4*>(srow + ic * 32 + g * 8);
+        if constexpr (HALF) sh[b] = *reinterpret_cast<const u32x2*>(srow + NC * 32 + g * 4);
+    }
+
+    // predecessor gathers; chunks past the tile (f >= NR * CPR) reload row 0 into
+    // the padding
 #pragma unroll
     for (int j = 0; j < TL::NJ; ++j) {
         const int f = j * 64 + lane;
         const int row = f < NR * CPR ? f / CPR : 0;
         const int slot = f - (f / CPR) * CPR;
         const int lc = (slot + CPR - row % CPR) % CPR;
-        int pid = 0, cidr = 0;
+        int pid = 0;
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
             const int x = __shfl(pred[b], row & 15);
-            const int y = __shfl(cid[b], row & 15);
-            if ((row >> 4) == b) { pid = x; cidr = y; }
+            if ((row >> 4) == b) pid = x;
         }
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(P + (int64_t)pid * R + lc * 8),
             (__attribute__((address_space(3))) void*)(sP + j * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(Sc + (int64_t)cidr * R + lc * 8),
-            (__attribute__((address_space(3))) void*)(sS + j * 512), 16, 0, 0);
     }
     // the row's KS projection partials and unary logits, straight to LDS as well
     // (partials: flat float4 f = 64 j + lane is partial f / (R / 4), ranks
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(64 * WAVES) void edges_bilinear(
             const int off = row * R + ((lcq + row) % CPR) * 8;
             float a[8];
             unpack8(*reinterpret_cast<const u32x4*>(sP + off), a);
-            bv[bq] = *reinterpret_cast<const u32x4*>(sS + off);
+            bv[bq] = sv[bq][ic];
 #pragma unroll
             for (int v = 0; v < 8; ++v) a[v] *= h[v];
             split3_bf16<8>(a, ahi[bq], amid[bq], alo[bq]);
@@ -317,7 +327,7 @@ __global__ __launch_bounds__(64 * WAVES) void edges_bilinear(
             const int row = bq * 16 + li;
             const int off = row * R + ((lcq + row) % CPR) * 8 + sub;
             const u32x2 x = *reinterpret_cast<const u32x2*>(sP + off);
-            bv[bq] = *reinterpret_cast<const u32x2*>(sS + off);
+            bv[bq] = sh[bq];
             float a[4] = {__uint_as_float(x[0] << 16) * hh[0], __uint_as_float(x[0] & 0xffff0000u) * hh[1],
                           __uint_as_float(x[1] << 16) * hh[2], __uint_as_float(x[1] & 0xffff0000u) * hh[3]};
             split3_bf16<4>(a, ahi[bq], amid[bq], alo[bq]);
