@@ -7,7 +7,9 @@ stream.  There is no fallback: if the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 
 import torch
@@ -106,6 +108,19 @@ def _dev(t: torch.Tensor, dtype, name: str) -> int:
     return t.data_ptr()
 
 
+def _on_stream(fn):
+    """Run a binding call with ``stream`` (when given) as torch's current stream,
+    so that the outputs and the workspace it allocates belong to the stream the
+    kernels run on: the caching allocator then reuses a freed workspace only
+    after the kernels queued on that stream."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kwargs):
+        ctx = contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, stream=stream, **kwargs)
+    return call
+
+
 def _workspace(nbytes: int, device, ws):
     if ws is None:
         return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
@@ -117,6 +132,7 @@ def lm_topk_workspace_size(T: int, V: int, Hd: int, k: int) -> int:
     return int(lib().dflash_lm_topk_workspace_size(T, V, Hd, k))
 
 
+@_on_stream
 def lm_topk(H: torch.Tensor, W: torch.Tensor, k: int, output_multiplier: float = 1.0,
             softcap: float = 0.0, ids: torch.Tensor | None = None,
             logits: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
@@ -139,6 +155,7 @@ def lm_topk(H: torch.Tensor, W: torch.Tensor, k: int, output_multiplier: float =
     return ids, logits
 
 
+@_on_stream
 def lm_topk_proj(H: torch.Tensor, W: torch.Tensor, k: int, output_multiplier: float, softcap: float,
                  W_proj: torch.Tensor, ids: torch.Tensor | None = None, logits: torch.Tensor | None = None,
                  hp: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
@@ -169,6 +186,7 @@ def candidate_edges_workspace_size(T: int, R: int, Hd: int) -> int:
     return int(lib().dflash_candidate_edges_workspace_size(T, R, Hd))
 
 
+@_on_stream
 def candidate_edges(pred_cb, succ_cb, cand_ids, unary, H, W_proj, anchor,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                     stream=None) -> torch.Tensor:
@@ -194,6 +212,7 @@ def candidate_edges(pred_cb, succ_cb, cand_ids, unary, H, W_proj, anchor,
     return out
 
 
+@_on_stream
 def candidate_edges_hp(pred_cb, succ_cb, cand_ids, unary, hp, anchor, out: torch.Tensor | None = None,
                        stream=None) -> torch.Tensor:
     """Edge scores ``[Rq, S, k, k]`` (fp32) from a given projection ``hp``
@@ -215,6 +234,7 @@ def candidate_edges_hp(pred_cb, succ_cb, cand_ids, unary, hp, anchor, out: torch
 
 
 # ---------------------------------------------------------------- q/k norm, RoPE, cache
+@_on_stream
 def rope_cos_sin(max_pos: int, D: int, theta: float, device, out=None, stream=None,
                  dtype=torch.float32) -> torch.Tensor:
     """``[max_pos, D]`` table (``D`` = the rotary dim): cos in ``[:, :D/2]``,
@@ -253,6 +273,7 @@ def _rope_args(cos_sin, D, rotary_dim, is_neox):
     return _dev(cos_sin, torch.bfloat16 if bf else torch.float32, "cos_sin"), rot, int(bool(is_neox)), int(bf)
 
 
+@_on_stream
 def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, positions, cos_sin,
                        slots=None, kv_cache=None, q_out=None, k_out=None, want_k: bool = True,
                        stream=None, rotary_dim: int | None = None, is_neox: bool = True,
@@ -290,6 +311,7 @@ def qk_norm_rope_cache(qkv, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, pos
 
 
 # ---------------------------------------------------------------- block attention
+@_on_stream
 def block_attn(q, kv_cache, block_tables, seq_lens, Lq: int, window: int, scale: float | None = None,
                out=None, workspace=None, stream=None, cache_fp8: str | None = None,
                kv_scale=None) -> torch.Tensor:
@@ -322,6 +344,7 @@ def context_kv_workspace_size(num_ctx: int, Hd: int) -> int:
     return int(lib().dflash_context_kv_workspace_size(num_ctx, Hd))
 
 
+@_on_stream
 def context_kv(ctx_states, hidden_norm_w, hidden_eps: float, W_kv, L: int, Hkv: int, D: int, k_norm_w,
                k_eps: float, positions, cos_sin, slots=None, caches=None, kv_out=None, want_kv: bool = False,
                workspace=None, stream=None, rotary_dim: int | None = None, is_neox: bool = True,
@@ -368,6 +391,7 @@ def context_kv(ctx_states, hidden_norm_w, hidden_eps: float, W_kv, L: int, Hkv: 
 
 
 # ---------------------------------------------------------------- draft-layer projections
+@_on_stream
 def linear(X, W, out=None, stream=None) -> torch.Tensor:
     """``bf16(X [M, K] . W [N, K]^T)`` (bias-free nn.Linear, fp32 accumulate)."""
     if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1]:
@@ -383,6 +407,7 @@ def linear(X, W, out=None, stream=None) -> torch.Tensor:
     return out
 
 
+@_on_stream
 def draft_attention(hidden, W_qkv, W_o, Hq: int, Hkv: int, D: int, q_w, k_w, eps: float, positions, cos_sin,
                     slots, kv_cache, block_tables, seq_lens, Lq: int, window: int, stream=None) -> torch.Tensor:
     """One draft attention sublayer (DFlash2BeamAttention.forward) on the

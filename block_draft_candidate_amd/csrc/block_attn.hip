@@ -17,10 +17,17 @@
 //   * S^T = K Q^T: v_mfma_f32_16x16x32_bf16, K rows from LDS, Q^T from registers;
 //     each lane then holds scores of a single query, so the online softmax
 //     (fp32, exp2) needs only two cross-lane steps.
-//   * O^T += V^T P^T: P^T comes straight from the S^T registers (bf16); V^T comes
-//     from the row-major V tile through ds_read_b64_tr_b16 (the transposing LDS
-//     read): lane p of a 16-lane group points at V[key(p / 4)][d0 + 4 (p % 4)],
-//     and lane i receives V[key(j)][d0 + i], j = 0..3.
+//   * O^T += V^T P^T: P^T comes straight from the S^T registers, split into two
+//     bf16 parts (hi = bf16(p), lo = bf16(p - hi)) so that two MFMAs carry p to
+//     2^-16 relative, the precision of the fp32 row sum that normalises it; V^T
+//     comes from the row-major V tile through ds_read_b64_tr_b16 (the
+//     transposing LDS read): lane p of a 16-lane group points at
+//     V[key(p / 4)][d0 + 4 (p % 4)], and lane i receives V[key(j)][d0 + i],
+//     j = 0..3.
+//   * Tile rows at or past the request's length (the unwritten rest of its last
+//     cache block, or that block again when a tile runs past it) are loaded
+//     from an out-of-range offset and land as zeros: their weight is zero, and
+//     a stale NaN or Inf there must not reach the output through 0 * NaN.
 //   * With an fp8 cache (E4M3fn or E5M2) the LDS-DMA brings the tile's
 //     256-byte fp8 rows into a ring of staging buffers instead, and after the
 //     tile's barrier the workgroup decodes them into one bf16 tile in the layout
@@ -41,6 +48,22 @@ constexpr int AT_BTCAP = 1024; // block-table entries staged in LDS (longer span
 constexpr int AT_ROW = 2 * AT_D;  // elements per cache row (K | V)
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// Two fp32 -> two bf16 packed (lo word = a), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t at_cvt_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// (a, b) = hi + lo with both parts bf16: hi = bf16(x), lo = bf16(x - hi).  x - hi
+// is exact in fp32 and |x - hi| <= ulp_bf16(x) / 2, so hi + lo is within
+// 2^-16 |x| of x.
+__device__ __forceinline__ void at_split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = at_cvt_bf16x2(a, b);
+    lo = at_cvt_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
 
 __device__ __forceinline__ void at_fence() { asm volatile("" ::: "memory"); }
 
@@ -143,6 +166,7 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
         }
     }
     constexpr int RPI = F8 == FP8_NONE ? 2 : 4;  // tile rows per DMA instruction
+    const int lrow = F8 == FP8_NONE ? (lane >> 5) : (lane >> 4);  // this lane's row within an instruction
     auto issue = [&](int tile, int st) {
         const int kb = kstart + tile * AT_TK;
 #pragma unroll
@@ -152,7 +176,8 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
             const uint8_t* blk = reinterpret_cast<const uint8_t*>(cache) + ((int64_t)b * Hkv + hk) * AT_BS * RB;
             void* dst = F8 == FP8_NONE ? (void*)(smem + st * AT_TK * AT_ROW + qd * 512)
                                        : (void*)(ring8 + st * AT_TK * AT_ROW + qd * 1024);
-            at_load_block_rows(blk, RB, loff[j], dst);
+            // rows at or past the request's length read as zeros (offset past the range)
+            at_load_block_rows(blk, RB, kb + RPI * qd + lrow < L ? loff[j] : (int)0x80000000, dst);
         }
     };
 
@@ -257,17 +282,19 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
                 lsum += pv[kblk][e];
             }
 
-        // O^T += V^T P^T over two 32-key steps; K index of the MFMA for lane group g,
+        // O^T += V^T P^T over 32-key steps; K index of the MFMA for lane group g,
         // element j <-> key 32 s2 + 4 g + j (j < 4) or 32 s2 + 16 + 4 g + (j - 4).
+        // P = P_hi + P_lo (two bf16 MFMAs), so the weights keep the row sum's precision.
         const int p = lane & 15;
 #pragma unroll
         for (int s2 = 0; s2 < AT_TK / 32; ++s2) {
-            u32x4 pp;
-            pp[0] = pack_bf16x2(pv[2 * s2][0], pv[2 * s2][1]);
-            pp[1] = pack_bf16x2(pv[2 * s2][2], pv[2 * s2][3]);
-            pp[2] = pack_bf16x2(pv[2 * s2 + 1][0], pv[2 * s2 + 1][1]);
-            pp[3] = pack_bf16x2(pv[2 * s2 + 1][2], pv[2 * s2 + 1][3]);
-            const bf16x8 pf = as_bf16x8(pp);
+            uint32_t ph[4], pl[4];
+            at_split_bf16x2(pv[2 * s2][0], pv[2 * s2][1], ph[0], pl[0]);
+            at_split_bf16x2(pv[2 * s2][2], pv[2 * s2][3], ph[1], pl[1]);
+            at_split_bf16x2(pv[2 * s2 + 1][0], pv[2 * s2 + 1][1], ph[2], pl[2]);
+            at_split_bf16x2(pv[2 * s2 + 1][2], pv[2 * s2 + 1][3], ph[3], pl[3]);
+            const bf16x8 pfh = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
+            const bf16x8 pfl = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
             const int r1 = 32 * s2 + 4 * g + (p >> 2);
             const int r2 = r1 + 16;
 #pragma unroll
@@ -282,7 +309,8 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
                     (__attribute__((address_space(3))) i16x4*)(tb + o2));
                 const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
                 const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), pf, o[mb], 0, 0, 0);
+                o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), pfl, o[mb], 0, 0, 0);
+                o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), pfh, o[mb], 0, 0, 0);
             }
         }
     }

@@ -18,6 +18,8 @@
 //      name.  a = P[pred] * h_p is formed in fp32 and split into three bf16 parts
 //      whose products with the bf16 successor rows are exact, so the k x k block
 //      comes out of bf16 MFMA with fp32 products and fp32 accumulation.
+#include <atomic>
+
 #include "common.h"
 
 namespace dflash {
@@ -390,9 +392,18 @@ static void launch_bilinear_r(const uint16_t* P, const uint16_t* Sc, const int32
     constexpr int wave_bytes = EdgeTile<KB, R, KS>::WAVE_BYTES;
     constexpr int WAVES = wave_bytes * 4 <= 64 * 1024 ? 4 : wave_bytes * 2 <= 64 * 1024 ? 2 : 1;
     static_assert(wave_bytes * WAVES <= 160 * 1024, "tile fits in LDS");
-    if (wave_bytes * WAVES > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&edges_bilinear<KB, R, KS, WAVES>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, wave_bytes * WAVES);
+    if (wave_bytes * WAVES > 64 * 1024) {
+        // the attribute is set once per device (bit d of `done`), not on every launch
+        static std::atomic<uint64_t> done{0};
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+        if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&edges_bilinear<KB, R, KS, WAVES>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, wave_bytes * WAVES) == hipSuccess)
+                done.fetch_or(bit, std::memory_order_release);
+        }
+    }
     hipLaunchKernelGGL((edges_bilinear<KB, R, KS, WAVES>), dim3((T + WAVES - 1) / WAVES), dim3(64 * WAVES),
                        wave_bytes * WAVES, st, P, Sc, ids, U, part, anchor, T, St, k, V, E);
 }
@@ -451,7 +462,9 @@ extern "C" int dflash_candidate_edges(const uint16_t* pred_cb, const uint16_t* s
     if (Rq < 1 || S < 1 || V < 1 || Hd < 1 || k < 1 || k > V || R < 1) return DFLASH_ERR_INVALID_ARG;
     if (k > 64 || R % 16 != 0 || R > 256 || Hd % 8 != 0) return DFLASH_ERR_UNSUPPORTED;
     const int64_t T = Rq * (int64_t)S;
-    if (T > INT32_MAX / 64 || V > INT32_MAX || Hd > (1 << 22)) return DFLASH_ERR_UNSUPPORTED;
+    if (T > INT32_MAX / 64 || V > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    // buffer ranges and lane offsets of the projection (up to 256 rows of Hd bf16) are int32 byte counts
+    if ((int64_t)256 * Hd * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     const EdgePlan p = edge_plan(T, R, Hd);
     if (ws_bytes < p.ws) return DFLASH_ERR_WORKSPACE;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -684,7 +684,9 @@ static int lm_topk_common(const uint16_t* H, const uint16_t* W, int64_t T, int64
     if (!(output_multiplier > 0.f) || !(output_multiplier < INFINITY)) return DFLASH_ERR_INVALID_ARG;
     if (softcap != softcap || softcap == INFINITY) return DFLASH_ERR_INVALID_ARG;
     if (k > 64 || Hd % 8 != 0) return DFLASH_ERR_UNSUPPORTED;
-    if (T > INT32_MAX || V > INT32_MAX || Hd > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    if (T > INT32_MAX || V > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    // tile buffer ranges and lane offsets (up to 256 rows of Hd bf16) are int32 byte counts
+    if ((int64_t)256 * Hd * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     LmPlan p;
     if (!lm_plan(T, V, Hd, k, p)) return DFLASH_ERR_UNSUPPORTED;
     if (ws_bytes < p.ws) return DFLASH_ERR_WORKSPACE;

@@ -260,15 +260,6 @@ def _rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     return x / np.sqrt(ms + eps) * w
 
 
-def _neox_rotate(y: np.ndarray, ang: np.ndarray) -> np.ndarray:
-    """Rotate pairs (i, i + D/2) of the last axis by ``ang`` (NeoX style)."""
-    D = y.shape[-1]
-    h = D // 2
-    c, s = np.cos(ang), np.sin(ang)
-    x1, x2 = y[..., :h], y[..., h:]
-    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
-
-
 def rope_cos_sin(positions, rotary_dim: int, theta: float, table: str = "f64"):
     """cos and sin of the RoPE angles ``[T, rotary_dim/2]`` (``rope_angles``
     with the rotary dim in the exponent).  ``table="bf16"`` rounds each value

@@ -71,6 +71,7 @@ def test_lm_topk_host_validation(L):
     assert call(c=float("nan"), wsb=ws) == 1
     assert call(k=65, V=4096, wsb=ws) == 2        # k > 64 unsupported
     assert call(Hd=260, wsb=ws) == 2              # Hd % 8
+    assert call(Hd=1 << 22, wsb=ws) == 2          # 256 rows of Hd bf16 overflow an int32 byte count
     assert call(wsb=ws - 1) == 3                  # workspace too small
     assert L.dflash_lm_topk_workspace_size(0, 1, 1, 1) == 0
 
@@ -91,6 +92,7 @@ def test_edges_host_validation(L):
     assert call(R=24) == 2          # R % 16
     assert call(R=512) == 2         # R > 256
     assert call(k=65, V=4096) == 2
+    assert call(Hd=1 << 22) == 2    # 256 rows of Hd bf16 overflow an int32 byte count
     assert call(wsb=ws - 4) == 3
 
 

@@ -7,7 +7,7 @@ import pytest
 
 from oracle import dflash_oracle as O
 import workloads as WL
-from tests.parity import assert_close
+from tests.parity import assert_close, check_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -110,10 +110,9 @@ def test_block_attn_fp8_cache(B, fmt, ks, vs):
     ref = O.block_attn(a["q"], codes, a["block_tables"], a["seq_lens"], a["query_len"], a["hq"], a["hkv"], D,
                        a["block_size"], a["window"], D ** -0.5, cache_fp8=fmt, k_scale=ks, v_scale=vs)
     g, r = O.bf16_to_f64(host_bf16(o)), O.bf16_to_f64(ref)
-    assert_close(g, r, f"fp8 {fmt} attention")
+    same, one_ulp, n = check_attention(g, r, f"fp8 {fmt} attention")
     rel = np.abs(g - r).max() / np.sqrt(np.mean(r * r))
-    say(f"[attn fp8 {fmt}] max|d|/rms(ref) = {rel:.3g}")
-    assert rel < 0.1
+    say(f"[attn fp8 {fmt}] equal {same} / within 1 ulp {one_ulp} / {n}; max|d|/rms(ref) = {rel:.3g}")
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
@@ -162,8 +161,8 @@ def test_draft_layer_with_an_fp8_cache(B):
     ro = O.block_attn(rq, rc, a["block_tables"], a["seq_lens"], a["query_len"], a["hq"], a["hkv"], D,
                       a["block_size"], a["window"], D ** -0.5, cache_fp8=fmt, k_scale=ks, v_scale=vs)
     g, r = O.bf16_to_f64(host_bf16(o)), O.bf16_to_f64(ro)
-    assert_close(g, r, "draft layer over an fp8 cache")
-    assert np.abs(g - r).max() / np.sqrt(np.mean(r * r)) < 0.1
+    # the two sides' q differ by rounding in a few elements: see the bf16 pipeline test
+    check_attention(g, r, "draft layer over an fp8 cache", pre_round=2.0 ** -10)
 
 
 def test_context_kv_fp8_with_rope_options(B):

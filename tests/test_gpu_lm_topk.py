@@ -5,7 +5,7 @@ import pytest
 
 from oracle import dflash_oracle as O
 import workloads as WL
-from tests.parity import check_topk_rows
+from tests.parity import check_topk_rows, check_topk_summaries
 
 pytestmark = pytest.mark.gpu
 
@@ -31,8 +31,7 @@ def _check(B, H, W, k, s, c, rows=None, label=""):
     gids, gvals = _run(B, H, W, k, s, c)
     rows = np.arange(H.shape[0]) if rows is None else np.asarray(rows)
     keys = O.lm_logit_keys(H, W, s, c, rows=rows)
-    rids, rvals = O.topk_from_keys(keys, k)
-    exact, near = check_topk_rows(gids[rows], gvals[rows], keys, rids, rvals, k)
+    exact, near = check_topk_rows(gids[rows], gvals[rows], keys, k, label=label)
     say(f"[lm_topk {label}] rows={len(rows)} exact={exact} near={near}")
     return gids, gvals
 
@@ -82,29 +81,36 @@ def test_one_hot_exact_at_full_vocab(B):
     assert np.array_equal(gids, rids) and np.array_equal(gvals, rvals)
 
 
-def test_full_workload_sampled_rows(B):
-    """The 256 x 16 workload in the launch configuration the benchmark times;
-    the oracle checks rows spread over every 256-row tile."""
+def _golden_all_rows(B, d, name):
+    """Every golden row of workload ``name`` (tests/golden/topk_<name>.npz,
+    written from the oracle by make_topk_goldens.py) against the GPU's top-k of
+    the whole workload, in the launch configuration the benchmark times."""
+    from tests.gpu_common import say
+    from tests.golden.make_topk_goldens import input_digest, load
+    rows, summ, k, V, digest = load(name)
+    assert input_digest(d) == digest, f"{name}: the seeded inputs are not the bits the goldens were made from"
+    assert k == d["top_k"] and V == d["vocab"]
+    gids, gvals = _run(B, d["H"], d["W"], k, d["multiplier"], d["softcap"])
+    exact, near = check_topk_summaries(gids[rows], gvals[rows], summ, k, V, label=name)
+    say(f"[lm_topk {name} golden] rows={len(rows)} exact={exact} near={near}")
+    return gids, gvals
+
+
+def test_full_workload_all_rows(B):
+    """All 4096 rows of the 256 x 16 workload against the oracle's goldens."""
     from tests.gpu_common import candidate
     d = candidate("full")
-    T = d["H"].shape[0]
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, T - 1], rng.integers(0, T, 27)]))
-    gids, gvals = _check(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"], rows, "full")
+    gids, gvals = _golden_all_rows(B, d, "full")
     # deterministic: a second call gives the same bits
     gids2, gvals2 = _run(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"])
     assert np.array_equal(gids, gids2) and np.array_equal(gvals.view(np.uint32), gvals2.view(np.uint32))
 
 
-def test_large_vocab_tie_heavy_sampled_rows(B):
+def test_large_vocab_tie_heavy_golden_requests(B):
     """The large configuration at its full 8192 rows (the launch the benchmark
-    times): 32 row tiles, k = 32, a tie-heavy LM head; rows from every fourth
-    row tile."""
-    d = WL.candidate_inputs("large")
-    T = d["H"].shape[0]
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, 255, 256, T - 1], np.arange(0, T, 1024) + rng.integers(0, 1024, T // 1024)]))
-    _check(B, d["H"], d["W"], d["top_k"], d["multiplier"], d["softcap"], rows, "large")
+    times): 32 row tiles, k = 32, a tie-heavy LM head; 32 whole requests, one in
+    every 256-row tile, against the oracle's goldens."""
+    _golden_all_rows(B, WL.candidate_inputs("large"), "large")
 
 
 @pytest.fixture(scope="module")
@@ -113,13 +119,24 @@ def full_inputs():
     return candidate("full")
 
 
+def _full_rows_vs_golden(B, d, r0, T, label):
+    """Rows r0 .. r0 + T - 1 of the full workload as a launch of their own,
+    every row against the oracle's goldens."""
+    from tests.gpu_common import say
+    from tests.golden.make_topk_goldens import load
+    rows, summ, k, V, _ = load("full")
+    assert np.array_equal(rows, np.arange(len(rows)))
+    H = np.ascontiguousarray(d["H"][r0:r0 + T])
+    gids, gvals = _run(B, H, d["W"], k, d["multiplier"], d["softcap"])
+    exact, near = check_topk_summaries(gids, gvals, summ[r0:r0 + T], k, V, label=label)
+    say(f"[lm_topk {label}] rows={T} exact={exact} near={near}")
+
+
 @pytest.mark.parametrize("T", [16, 33, 64])
 def test_skinny_rows_full_vocab(B, full_inputs, T):
     """Up to 64 rows the head runs 64-row tiles: every row of the full
     vocabulary's product against the oracle, 16 / 33 (a ragged tile) / 64."""
-    d = full_inputs
-    H = np.ascontiguousarray(d["H"][(T * 37) % 1000:][:T])
-    _check(B, H, d["W"], d["top_k"], d["multiplier"], d["softcap"], label=f"skinny T{T}")
+    _full_rows_vs_golden(B, full_inputs, (T * 37) % 1000, T, f"skinny T{T}")
 
 
 @pytest.mark.parametrize("T,V,Hd,k", [
@@ -133,9 +150,6 @@ def test_skinny_ragged(B, T, V, Hd, k):
 
 def test_256_rows_full_vocab(B, full_inputs):
     """256 rows over the full vocabulary (one row tile, 256 groups of 256
-    columns, two merge levels): the benchmark's bandwidth-regime launch."""
-    d = full_inputs
-    H = np.ascontiguousarray(d["H"][:256])
-    rng = np.random.default_rng(256)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255], rng.integers(0, 256, 19)]))
-    _check(B, H, d["W"], d["top_k"], d["multiplier"], d["softcap"], rows, "256 rows full vocab")
+    columns, two merge levels): the benchmark's bandwidth-regime launch, every
+    row against the oracle's goldens."""
+    _full_rows_vs_golden(B, full_inputs, 0, 256, "256 rows full vocab")

@@ -6,7 +6,7 @@ import pytest
 
 from oracle import dflash_oracle as O
 import workloads as WL
-from tests.parity import assert_close
+from tests.parity import ATTN_PRE_ROUND, assert_close, check_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -103,13 +103,12 @@ def _ref_attn(a, window=None):
                         a["hkv"], D, a["block_size"], a["window"] if window is None else window, D ** -0.5)
 
 
-def _check_attn(got, ref, label):
+def _check_attn(got, ref, label, pre_round=ATTN_PRE_ROUND):
     from tests.gpu_common import say
     g, r = O.bf16_to_f64(got), O.bf16_to_f64(ref)
-    assert_close(g, r, label)
+    same, one_ulp, n = check_attention(g, r, label, pre_round)
     rel = np.abs(g - r).max() / np.sqrt(np.mean(r * r))
-    say(f"[attn {label}] max|d|/rms(ref) = {rel:.3g}")
-    assert rel < 0.1
+    say(f"[attn {label}] equal {same} / within 1 ulp {one_ulp} / {n}; max|d|/rms(ref) = {rel:.3g}")
 
 
 @pytest.mark.parametrize("q_scale", [1.0, 4.0])
@@ -177,4 +176,91 @@ def test_pipeline_qk_then_attention(B):
                                          a["positions"], a["theta"], a["slots"], a["cache"], a["block_size"])
     ref = O.block_attn(rq, rcache, a["block_tables"], a["seq_lens"], a["query_len"], a["hq"], a["hkv"], D,
                        a["block_size"], a["window"], D ** -0.5)
-    _check_attn(host_bf16(o), ref, "qk -> attn")
+    # the two sides' q differ by rounding in a few elements (counted by the q/k
+    # tests): one ulp of a q element (2^-8 relative, |q k| <= ~16, scale 2^-3.5)
+    # moves that head's scores by up to ~5e-3 and its outputs by up to ~1e-3
+    _check_attn(host_bf16(o), ref, "qk -> attn", pre_round=2.0 ** -10)
+
+
+def _plant_window_edges(a, value=50.0):
+    """Cache copy whose V rows (every kv head) hold +-value at the keys around
+    each query's window edge: its first visible key, the key just below it, and
+    the request's last key.  A key wrongly in or out of one query's window then
+    moves that query's output by about value / (visible keys) in every element."""
+    cache = a["cache"].copy()
+    D, bs, Lq, W = a["head_dim"], a["block_size"], a["query_len"], a["window"]
+    plus, minus = WL.to_bf16_bits(np.float32([value, -value]))
+    planted = 0
+    for r in range(a["requests"]):
+        L = int(a["seq_lens"][r])
+        marks = {L - 1}
+        for i in range(Lq):
+            lo = L - Lq + i - W + 1
+            marks.update(x for x in (lo - 1, lo) if x >= 0)
+        for j in marks:
+            b, o = divmod(j, bs)
+            cache[a["block_tables"][r, b], :, o, D:] = plus if j % 2 == 0 else minus
+        planted += len(marks)
+    return cache, planted
+
+
+def test_attention_window_edges_planted(B):
+    """Large V rows at every query's window edge (R17: the window keeps the W
+    keys at or before the query's position; later keys of the block are all
+    visible): an off-by-one at either end, or a lost last key, fails."""
+    from tests.gpu_common import say
+    a = WL.attention_inputs("attn", requests=32)
+    cache, planted = _plant_window_edges(a)
+    a = dict(a, cache=cache)
+    edged = int(np.sum(a["seq_lens"] - a["query_len"] - a["window"] + 1 > 0))
+    say(f"[attn planted] {planted} planted keys; {edged} of {a['requests']} requests have a window edge")
+    assert edged >= a["requests"] // 2
+    _check_attn(_attn(B, a), _ref_attn(a), "window edges planted")
+    # the planted rows matter: the same window one key wider changes the outputs
+    wider = _ref_attn(a, window=a["window"] + 1)
+    assert not np.array_equal(wider, _ref_attn(a))
+
+
+def _nan_unwritten(a):
+    """Cache copy whose rows at positions >= seq_len in each request's last block
+    (never written) hold NaN."""
+    cache = a["cache"].copy()
+    bs = a["block_size"]
+    nan = WL.to_bf16_bits(np.float32([np.nan]))[0]
+    n = 0
+    for r in range(a["requests"]):
+        L = int(a["seq_lens"][r])
+        if L % bs:
+            cache[a["block_tables"][r, (L - 1) // bs], :, L % bs:, :] = nan
+            n += bs - L % bs
+    return cache, n
+
+
+@pytest.mark.parametrize("fmt", [None, "e4m3", "e5m2"])
+def test_attention_ignores_unwritten_slots(B, fmt):
+    """The rows past each request's length in its last cache block are never
+    written (a stale NaN or Inf may sit there); the attention must not read them
+    into the output: equal to the oracle, which reads only written rows."""
+    import torch
+    from tests.gpu_common import dev, dev_bf16, host_bf16, say
+    a = WL.attention_inputs("attn", requests=16)
+    cache, n = _nan_unwritten(a)
+    assert n > 0
+    D = a["head_dim"]
+    args = (dev(a["block_tables"]), dev(a["seq_lens"]), a["query_len"], a["window"])
+    if fmt is None:
+        o = B.block_attn(dev_bf16(a["q"]), dev_bf16(cache), *args)
+        ref = O.block_attn(a["q"], cache, a["block_tables"], a["seq_lens"], a["query_len"], a["hq"], a["hkv"], D,
+                           a["block_size"], a["window"], D ** -0.5)
+    else:
+        ks, vs = 0.0078125, 0.0625
+        codes = np.empty(cache.shape, np.uint8)
+        codes[..., :D] = O.bf16_to_fp8_scaled(cache[..., :D], ks, fmt)
+        codes[..., D:] = O.bf16_to_fp8_scaled(cache[..., D:], vs, fmt)
+        sc = torch.tensor([ks, vs], dtype=torch.float32, device="cuda")
+        o = B.block_attn(dev_bf16(a["q"]), dev(codes), *args, cache_fp8=fmt, kv_scale=sc)
+        ref = O.block_attn(a["q"], codes, a["block_tables"], a["seq_lens"], a["query_len"], a["hq"], a["hkv"], D,
+                           a["block_size"], a["window"], D ** -0.5, cache_fp8=fmt, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    say(f"[attn unwritten NaN {fmt}] {n} NaN rows per kv head")
+    _check_attn(host_bf16(o), ref, f"NaN in unwritten rows ({fmt or 'bf16'})")
