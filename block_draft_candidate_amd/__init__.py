@@ -15,7 +15,7 @@ import os
 import torch
 
 __all__ = [
-    "DFlashError", "lib", "lm_topk", "lm_topk_workspace_size", "lm_topk_proj", "candidate_edges",
+    "DFlashError", "lib", "lm_topk", "lm_topk_workspace_size", "lm_topk_noalloc", "lm_topk_proj", "candidate_edges",
     "candidate_edges_workspace_size", "candidate_edges_hp", "rope_cos_sin", "qk_norm_rope_cache", "block_attn",
     "context_kv", "context_kv_workspace_size", "linear", "draft_attention", "LIB_PATH",
 ]
@@ -31,6 +31,8 @@ _SIGS = {
     "dflash_lm_topk_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32]),
     "dflash_lm_topk": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32,
                                       _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "dflash_lm_topk_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32,
+                                              _c_p, _c_p, _c_p]),
     "dflash_lm_topk_proj": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32,
                                            _c_p, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dflash_candidate_edges_workspace_size": (_c_sz, [_c_i64, _c_i32, _c_i64]),
@@ -152,6 +154,28 @@ def lm_topk(H: torch.Tensor, W: torch.Tensor, k: int, output_multiplier: float =
                               _dev(ids, torch.int32, "ids"), _dev(logits, torch.float32, "logits"),
                               ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "dflash_lm_topk")
+    return ids, logits
+
+
+@_on_stream
+def lm_topk_noalloc(H: torch.Tensor, W: torch.Tensor, k: int, output_multiplier: float = 1.0,
+                    softcap: float = 0.0, ids: torch.Tensor | None = None,
+                    logits: torch.Tensor | None = None, stream=None):
+    """``lm_topk`` whose scratch is the library's own device array (the C call
+    allocates nothing; pass ``ids`` and ``logits`` to allocate nothing here
+    either).  Calls that overlap on one GPU race on that array."""
+    T, Hd = H.shape
+    V = W.shape[0]
+    if W.shape[1] != Hd:
+        raise ValueError("H and W disagree on the hidden size")
+    dev = H.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    logits = torch.empty((T, k), dtype=torch.float32, device=dev) if logits is None else logits
+    st = lib().dflash_lm_topk_noalloc(_dev(H, torch.bfloat16, "H"), _dev(W, torch.bfloat16, "W"), T, V, Hd, k,
+                                      float(output_multiplier), float(softcap),
+                                      _dev(ids, torch.int32, "ids"), _dev(logits, torch.float32, "logits"),
+                                      _stream(stream))
+    _check(st, "dflash_lm_topk_noalloc")
     return ids, logits
 
 

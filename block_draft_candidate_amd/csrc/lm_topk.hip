@@ -25,6 +25,9 @@
 //     H slices to several groups.
 //   * A merge kernel picks the k best of the groups' partial lists per row
 //     (with more than 16 groups, after levels that merge blocks of 16 lists).
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 
 namespace dflash {
@@ -675,11 +678,12 @@ extern "C" size_t dflash_lm_topk_workspace_size(int64_t T, int64_t V, int64_t Hd
     return p.ws;
 }
 
-static int lm_topk_common(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd, int32_t k,
-                          float output_multiplier, float softcap, int32_t* ids, float* logits, void* ws,
-                          size_t ws_bytes, const LmProj& pj, void* stream) {
-    if (!H || !W || !ids || !logits || !ws) return DFLASH_ERR_INVALID_ARG;
-    if (!DFLASH_ALIGNED16(H) || !DFLASH_ALIGNED16(W) || !DFLASH_ALIGNED16(ws)) return DFLASH_ERR_INVALID_ARG;
+// Host checks of the arguments every LM-head call shares (no HIP call); fills
+// the launch plan.
+static int lm_topk_validate(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd, int32_t k,
+                            float output_multiplier, float softcap, int32_t* ids, float* logits, LmPlan& p) {
+    if (!H || !W || !ids || !logits) return DFLASH_ERR_INVALID_ARG;
+    if (!DFLASH_ALIGNED16(H) || !DFLASH_ALIGNED16(W)) return DFLASH_ERR_INVALID_ARG;
     if (T < 1 || V < 1 || Hd < 1 || k < 1 || k > V) return DFLASH_ERR_INVALID_ARG;
     if (!(output_multiplier > 0.f) || !(output_multiplier < INFINITY)) return DFLASH_ERR_INVALID_ARG;
     if (softcap != softcap || softcap == INFINITY) return DFLASH_ERR_INVALID_ARG;
@@ -687,9 +691,13 @@ static int lm_topk_common(const uint16_t* H, const uint16_t* W, int64_t T, int64
     if (T > INT32_MAX || V > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     // tile buffer ranges and lane offsets (up to 256 rows of Hd bf16) are int32 byte counts
     if ((int64_t)256 * Hd * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
-    LmPlan p;
     if (!lm_plan(T, V, Hd, k, p)) return DFLASH_ERR_UNSUPPORTED;
-    if (ws_bytes < p.ws) return DFLASH_ERR_WORKSPACE;
+    return DFLASH_OK;
+}
+
+static int lm_topk_launch(const LmPlan& p, const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd,
+                          int32_t k, float output_multiplier, float softcap, int32_t* ids, float* logits, void* ws,
+                          const LmProj& pj, void* stream) {
     const float c = softcap > 0.f ? softcap : 0.f;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     uint64_t* part = reinterpret_cast<uint64_t*>(ws);
@@ -703,6 +711,17 @@ static int lm_topk_common(const uint16_t* H, const uint16_t* W, int64_t T, int64
     }
     DFLASH_LAUNCH_CHECK();
     return DFLASH_OK;
+}
+
+static int lm_topk_common(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd, int32_t k,
+                          float output_multiplier, float softcap, int32_t* ids, float* logits, void* ws,
+                          size_t ws_bytes, const LmProj& pj, void* stream) {
+    if (!ws || !DFLASH_ALIGNED16(ws)) return DFLASH_ERR_INVALID_ARG;
+    LmPlan p;
+    const int st = lm_topk_validate(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, p);
+    if (st != DFLASH_OK) return st;
+    if (ws_bytes < p.ws) return DFLASH_ERR_WORKSPACE;
+    return lm_topk_launch(p, H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, ws, pj, stream);
 }
 
 extern "C" int dflash_lm_topk(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd,
@@ -721,4 +740,57 @@ extern "C" int dflash_lm_topk_proj(const uint16_t* H, const uint16_t* W, int64_t
     if (R > 4096 || (int64_t)R * Hd * 2 > INT32_MAX || T * (int64_t)R * 4 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     return lm_topk_common(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, ws, ws_bytes,
                           LmProj{W_proj, R, hp}, stream);
+}
+
+// ---------------------------------------------------------------------------
+// dflash_lm_topk_noalloc: the same kernels with their partial lists in a
+// library-owned device array instead of a caller workspace, for callers that
+// cannot allocate.
+//
+// `scratch` is a file-scope device array: every GPU the library runs on holds
+// its own copy until the process ends.  In host code its name is only a
+// host-side stand-in, never a device address; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current (on the
+// entry point's first call there) and kept in lm_scratch_ptr.  Every call on a
+// GPU shares that GPU's array and it keeps the last call's contents; nothing in
+// it has to start at zero (each workgroup writes every entry of its lists before
+// the merge reads them).  Calls that overlap on one GPU race on the array.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[DFLASH_LM_TOPK_SCRATCH_BYTES];
+
+namespace {
+constexpr int LM_SCRATCH_MAX_DEVICES = 64;
+std::atomic<void*> lm_scratch_ptr[LM_SCRATCH_MAX_DEVICES];
+std::mutex lm_scratch_mu;
+
+// Device address of `scratch` on the current device.
+int lm_scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= LM_SCRATCH_MAX_DEVICES) return DFLASH_ERR_HIP;
+    void* ptr = lm_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(lm_scratch_mu);
+        ptr = lm_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DFLASH_ERR_HIP;
+            lm_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return DFLASH_OK;
+}
+}  // namespace
+
+extern "C" int dflash_lm_topk_noalloc(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd,
+                                      int32_t k, float output_multiplier, float softcap, int32_t* ids,
+                                      float* logits, void* stream) {
+    LmPlan p;
+    int st = lm_topk_validate(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, p);
+    if (st != DFLASH_OK) return st;
+    if (p.ws > DFLASH_LM_TOPK_SCRATCH_BYTES) return DFLASH_ERR_SCRATCH;
+    void* ws = nullptr;
+    st = lm_scratch_address(&ws);
+    if (st != DFLASH_OK) return st;
+    return lm_topk_launch(p, H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, ws,
+                          LmProj{nullptr, 0, nullptr}, stream);
 }

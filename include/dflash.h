@@ -28,7 +28,9 @@
  *     stride argument says otherwise.  Every pointer must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *     work on that stream: they never synchronise and never allocate.  Scratch
- *     memory comes from the caller (`ws`, sized by the *_workspace_size query).
+ *     memory comes from the caller (`ws`, sized by the *_workspace_size query),
+ *     except for dflash_lm_topk_noalloc, whose scratch is a fixed device array
+ *     of the library (see there).
  *   - The library keeps no state between calls; calls on different streams
  *     may run concurrently if their output buffers and workspaces differ.
  *   - Return value: a dflash_status.  On any non-OK status nothing was enqueued,
@@ -53,7 +55,8 @@ typedef enum {
     DFLASH_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, k > vocab ... */
     DFLASH_ERR_UNSUPPORTED = 2, /* a size the library does not handle (see each call) */
     DFLASH_ERR_WORKSPACE = 3,   /* ws smaller than the *_workspace_size query */
-    DFLASH_ERR_HIP = 4          /* a HIP launch failed */
+    DFLASH_ERR_HIP = 4,         /* a HIP launch failed */
+    DFLASH_ERR_SCRATCH = 5      /* a no-alloc call needs more than the library's static scratch */
 } dflash_status;
 
 /* Human-readable text of a status code (static storage). */
@@ -79,7 +82,7 @@ int dflash_version(void);
  *   logits  fp32  [T, k]      output
  *   ws      workspace of dflash_lm_topk_workspace_size(T, V, Hd, k) bytes
  *
- * Requirements: T, V, Hd >= 1; Hd % 8 == 0; 1 <= k <= min(V, 64);
+ * Requirements: T, V, Hd >= 1; Hd % 8 == 0, Hd < 2^22; 1 <= k <= min(V, 64);
  * output_multiplier finite and > 0; softcap <= 0 (off) or finite.
  * The result does not depend on the stream, workspace contents or timing
  * (deterministic).
@@ -90,6 +93,31 @@ int dflash_lm_topk(const uint16_t* H, const uint16_t* W,
                    float output_multiplier, float softcap,
                    int32_t* ids, float* logits,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dflash_lm_topk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and requirements
+ * as dflash_lm_topk (bit-identical outputs: the same kernels), minus ws.
+ *
+ * The partial lists go to a device array of the library,
+ * DFLASH_LM_TOPK_SCRATCH_BYTES (16 MiB) per GPU, held until the process ends.
+ * The call allocates nothing.  Its first call on a device looks up that
+ * device's address of the array (hipGetSymbolAddress), so call it with the
+ * device of H, W, ids, logits and the stream current.  All calls on one GPU
+ * share the array: calls that overlap on one GPU (different streams, or
+ * threads without ordering) race and give undefined results; serialise them,
+ * e.g. on one stream.  Nothing in the array needs clearing between calls.
+ *
+ * Returns DFLASH_ERR_SCRATCH, before anything is enqueued, when
+ * dflash_lm_topk_workspace_size(T, V, Hd, k) exceeds the array (e.g. T = 8192
+ * rows at k = 32 fit exactly; more do not).
+ * ---------------------------------------------------------------------- */
+#define DFLASH_LM_TOPK_SCRATCH_BYTES ((size_t)16 << 20)
+int dflash_lm_topk_noalloc(const uint16_t* H, const uint16_t* W,
+                           int64_t T, int64_t V, int64_t Hd, int32_t k,
+                           float output_multiplier, float softcap,
+                           int32_t* ids, float* logits, void* stream);
 
 /* ------------------------------------------------------------------------
  * Candidate-selector edge scores (DFlash2BeamCandidateSelector).
@@ -109,7 +137,7 @@ int dflash_lm_topk(const uint16_t* H, const uint16_t* W,
  *   ws                dflash_candidate_edges_workspace_size(Rq*S, R, Hd) bytes
  *
  * Requirements: Rq, S, V >= 1; 1 <= k <= min(V, 64); R % 16 == 0, 16 <= R <= 256;
- * Hd % 8 == 0, Hd <= 2^22.  Ids and anchors outside [0, V) are clamped into range.
+ * Hd % 8 == 0, Hd < 2^22.  Ids and anchors outside [0, V) are clamped into range.
  * Deterministic; edges[r, 0, q, :] is bit-identical for every q.
  * ---------------------------------------------------------------------- */
 size_t dflash_candidate_edges_workspace_size(int64_t T, int32_t R, int64_t Hd);

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(5):
+    for code in range(6):
         assert L.dflash_status_string(code)
     assert L.dflash_status_string(99) == b"unknown status"
     assert L.dflash_version() >= 100
@@ -74,6 +74,23 @@ def test_lm_topk_host_validation(L):
     assert call(Hd=1 << 22, wsb=ws) == 2          # 256 rows of Hd bf16 overflow an int32 byte count
     assert call(wsb=ws - 1) == 3                  # workspace too small
     assert L.dflash_lm_topk_workspace_size(0, 1, 1, 1) == 0
+
+
+def test_lm_topk_noalloc_host_validation(L):
+    """The no-alloc call checks its arguments like dflash_lm_topk and rejects a
+    problem whose partial lists exceed the library's 16 MiB scratch, all on the
+    host before any HIP call."""
+    f = L.dflash_lm_topk_noalloc
+
+    def call(T=8, V=1024, Hd=256, k=4, ids=FAKE):
+        return f(FAKE, FAKE, T, V, Hd, k, 1.0, 0.0, ids, FAKE, None)
+
+    assert call(ids=None) == 1
+    assert call(k=0) == 1
+    assert call(Hd=260) == 2
+    assert L.dflash_lm_topk_workspace_size(8192, 20000, 64, 32) == 16 << 20   # fits exactly
+    assert L.dflash_lm_topk_workspace_size(8193, 20000, 64, 32) > 16 << 20
+    assert call(T=8193, V=20000, Hd=64, k=32) == 5                             # DFLASH_ERR_SCRATCH
 
 
 def test_edges_host_validation(L):
