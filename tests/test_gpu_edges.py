@@ -79,6 +79,10 @@ def test_large_full_size_sampled_requests(B):
     (2, 3, 40, 500, 256, 64),     # k in (32, 64], R = 256
     (1, 1, 1, 10, 32, 8),         # one request, one step, k = 1
     (77, 3, 16, 2000, 128, 4104), # ragged row count for the projection tiles
+    (32, 16, 16, 5000, 128, 1000),  # 8 row blocks x 4 slices, Hd % 64 != 0
+    (20, 7, 11, 3000, 48, 264),     # ragged rows, rank % 32 != 0, a short last slice
+    (64, 16, 16, 7000, 80, 512),    # 16 row blocks, rank 80
+    (2, 4, 4, 1024, 16, 256),       # rank 16, one row block
 ])
 def test_shapes(B, Rq, S, k, V, R, Hd):
     rng = np.random.default_rng(Rq * 1000 + k)
@@ -100,3 +104,4 @@ def test_zero_codebooks_give_unary(B):
 def test_deterministic(B):
     d = WL.candidate_inputs("mid")
     assert np.array_equal(_gpu_edges(B, d).view(np.uint32), _gpu_edges(B, d).view(np.uint32))
+
