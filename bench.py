@@ -171,37 +171,70 @@ def traffic_for(kernel):
     return None
 
 
-def cpu_baseline(cand, attn, edges_per_step, frac):
-    """The oracle timed on a bounded sample of the step: 1/frac of its
-    candidate-head requests and of its attention requests (64 of 256 and 32 of
-    128 at the default 1/4), scaled to a whole step."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_step_sample(cand, attn, nr, na):
+    """The oracle over nr candidate-head requests (LM-head top-k + edges) and na
+    attention requests (q/k norm + RoPE + cache, then attention); seconds."""
     import numpy as np
     from oracle import dflash_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
     S, k = cand["steps"], cand["top_k"]
-    nr = max(1, cand["requests"] // frac)
     rows = np.arange(nr * S)
     t0 = time.perf_counter()
     ids, vals = O.lm_topk(cand["H"], cand["W"], k, cand["multiplier"], cand["softcap"], rows=rows)
     O.candidate_edges(cand["P"], cand["S"], ids.reshape(nr, S, k), vals.reshape(nr, S, k), cand["H"][rows],
                       cand["Wp"], cand["anchor"][:nr])
     Lq, D = attn["query_len"], attn["head_dim"]
-    na = max(1, attn["requests"] // frac)
     q, _, c2 = O.qk_norm_rope_cache(attn["qkv"][:na * Lq], attn["hq"], attn["hkv"], D, attn["q_w"], attn["k_w"],
                                     attn["eps"], attn["positions"][:na * Lq], attn["theta"],
                                     attn["slots"][:na * Lq], attn["cache"], attn["block_size"])
     O.block_attn(q, c2, attn["block_tables"][:na], attn["seq_lens"][:na], Lq, attn["hq"], attn["hkv"], D,
                  attn["block_size"], attn["window"], D ** -0.5)
-    dt = time.perf_counter() - t0
-    return {"value": edges_per_step / (dt * frac), "unit": "edge scores/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{nr} of {cand['requests']} candidate-head requests ({nr * S} rows: LM-head top-k + edges) "
-                      f"and {na} of {attn['requests']} attention requests (qk-norm/RoPE/cache + attention) = "
-                      f"1/{frac} of a step; {dt:.1f} s on the host, scaled to a whole step"}
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(cand, attn, edges_per_step, frac):
+    """The oracle timed on a bounded sample of the step: 1/frac of its
+    candidate-head requests and of its attention requests (64 of 256 and 32 of
+    128 at the default 1/4), scaled to a whole step, with every host core; and
+    on 1/64 of the step (4 and 2 requests) with one thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        cores = len(os.sched_getaffinity(0))
+    nr = max(1, cand["requests"] // frac)
+    na = max(1, attn["requests"] // frac)
+    dt = oracle_step_sample(cand, attn, nr, na)
+    single = None
+    if threadpool_limits is not None:
+        f1 = 64
+        nr1, na1 = max(1, cand["requests"] // f1), max(1, attn["requests"] // f1)
+        with threadpool_limits(limits=1):
+            dt1 = oracle_step_sample(cand, attn, nr1, na1)
+        s1 = cand["requests"] / nr1  # the sample is 1/s1 of the step's candidate head (and attention)
+        single = {"value": edges_per_step / (dt1 * s1), "unit": "edge scores/s", "cores": 1,
+                  "sample": f"{nr1} candidate-head and {na1} attention requests = 1/{s1:g} of a step, one BLAS "
+                            f"thread: {dt1:.1f} s, scaled to a whole step"}
+    scale = cand["requests"] / nr
+    return {"value": edges_per_step / (dt * scale), "unit": "edge scores/s", "cores": int(cores),
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{nr} of {cand['requests']} candidate-head requests ({nr * cand['steps']} rows: LM-head "
+                      f"top-k + edges) and {na} of {attn['requests']} attention requests (qk-norm/RoPE/cache + "
+                      f"attention) = 1/{scale:g} of a step; {dt:.1f} s on the host with {cores} BLAS threads, scaled "
+                      "to a whole step",
+            "single_thread": single}
 
 
 def main():
@@ -294,7 +327,7 @@ def main():
 
     names = ["lm_topk", "edges", "qk", "attn"]
     ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
-    acc_ms = {n: 0.0 for n in names}
+    acc_ms = {n: [] for n in names}
 
     def step(timed):
         def call(n, fn):
@@ -318,7 +351,7 @@ def main():
         if timed:
             torch.cuda.synchronize()
             for n in names:
-                acc_ms[n] += ev[n][0].elapsed_time(ev[n][1])
+                acc_ms[n].append(ev[n][0].elapsed_time(ev[n][1]))
 
     log(f"warmup {args.warmup} ...")
     for _ in range(args.warmup):
@@ -338,7 +371,8 @@ def main():
     # per-kernel HIP-event times over the same number of steps
     for _ in range(args.steps):
         step(True)
-    kms = {n: acc_ms[n] / args.steps for n in names}
+    kms = {n: sum(acc_ms[n]) / len(acc_ms[n]) for n in names}
+    kstat = {n: {"ms_median": sorted(acc_ms[n])[len(acc_ms[n]) // 2], "ms_min": min(acc_ms[n])} for n in names}
 
     edges_per_step = Rq * S * k * k
     value = edges_per_step / (ms_per_step / 1e3)
@@ -631,6 +665,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    # the step's four calls: mean (the figures above), median and min over the event-timed steps
+    for key, n in (("lm_topk", "lm_topk"), ("edges", "edges"), ("qk_norm_rope_cache", "qk"), ("block_attn", "attn")):
+        result["kernels"][key].update(kstat[n])
     if ctx_kernel is not None:
         result["kernels"]["context_kv"] = ctx_kernel
     result["kernels"].update(lin_kernels)
