@@ -568,15 +568,183 @@ __global__ __launch_bounds__(256) void lm_topk_merge16_level(const uint64_t* __r
     }
 }
 
+// ---------------------------------------------------------------------------
+// lm_topk_skinny: the LM head for at most 16 rows, where the contraction is a
+// stream over W with little arithmetic per byte (16 rows: 16 flop per W byte).
+//
+// Workgroup g (one per CU) owns a contiguous run of 16-row vocabulary tiles;
+// its 8 waves take every 8th tile of the run.  A wave streams its tiles' W rows
+// from HBM straight into registers, PF fragments of 16 bytes per lane ahead of
+// the MFMA that uses them (8 waves x PF KB in flight per CU), so no LDS ring
+// and no barrier sits in the stream.  The <= 16 hidden rows are loaded into
+// LDS once (rows padded by 16 bytes, so the 16 rows of a fragment read fall on
+// different banks).  v_mfma_f32_16x16x32_bf16 with the vocabulary rows as M and
+// the hidden rows as N: after a tile's last K step lane (j, g) holds the
+// logits of hidden row j for the tile's vocabulary rows 4g .. 4g + 3; it keys
+// them (scale, cap, bf16) and keeps its own sorted list of the best KCAP keys of
+// row j.  At the end the 32 lists of each row (8 waves x 4 lane groups) are
+// merged in LDS into the group's partial list, the tile kernel's format, and
+// lm_topk_merge16(_level) merge the groups as for the tile kernel.
+// ---------------------------------------------------------------------------
+constexpr int SK_THREADS = 512;
+constexpr int SK_WAVES = SK_THREADS / 64;
+constexpr int SK_MAXHD = 4096;                  // the hidden rows fill 128 KB of LDS at most
+constexpr int SK_PITCH_PAD = 8;                 // bf16 elements of padding per hidden row
+constexpr int SK_LDS = 16 * (SK_MAXHD + SK_PITCH_PAD);  // elements; also holds the final 16 x 32 x KCAP lists
+
+template <int KCAP, int PF>
+__global__ __launch_bounds__(SK_THREADS) void lm_topk_skinny(const uint16_t* __restrict__ H,
+                                                             const uint16_t* __restrict__ W, int T, int V, int Hd,
+                                                             int ntiles, int G, float s, float c, float inv_c,
+                                                             uint64_t* __restrict__ part) {
+    static_assert(16 * 32 * KCAP * 2 <= SK_LDS, "the row lists fit the LDS of the hidden rows");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[SK_LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = blockIdx.x;
+    const int t0 = (int)((int64_t)grp * ntiles / G), t1 = (int)((int64_t)(grp + 1) * ntiles / G);
+    const int v0 = t0 * 16;  // the group's first vocabulary row: ids are v0 + column
+    const int pitch = Hd + SK_PITCH_PAD;
+
+    // the hidden rows (rows >= T read as zero) -> LDS
+    const int c8n = Hd / 8;
+    for (int idx = tid; idx < 16 * c8n; idx += SK_THREADS) {
+        const int r = idx / c8n, c8 = idx - r * c8n;
+        const u32x4 v = r < T ? ldg16(H + (int64_t)r * Hd + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(lds + r * pitch + c8 * 8) = v;
+    }
+    __syncthreads();
+
+    const int j = lane & 15, g = lane >> 4;
+    const int nK = Hd / 32;          // MFMA K steps per tile
+    const int nKB = nK / PF;         // blocks of PF steps per tile
+    const int nt = t1 - t0;
+    const int ntw = nt > wave ? (nt - wave + SK_WAVES - 1) / SK_WAVES : 0;  // this wave's tiles
+    const int nblk = ntw * nKB;
+    // W fragment of lane (j, g) at block b, step i: row (tile's first row + j), columns
+    // 32 (kb + i) + 8 g .. + 8; rows past the vocabulary reload the last row (discarded)
+    auto frag_ptr = [&](int b) {
+        const int bb = min(b, max(nblk - 1, 0));
+        const int tw = bb / nKB;
+        const int kb = (bb - tw * nKB) * PF;
+        const int v = min((t0 + wave + SK_WAVES * tw) * 16 + j, V - 1);
+        return W + (int64_t)v * Hd + kb * 32 + 8 * g;
+    };
+    u32x4 buf[PF];
+    {
+        // issued in the order the loop consumes them (the loop's waits then
+        // leave PF - 1 fragments in flight; issued in another order, the wait
+        // at the loop head would drain them all)
+        const uint16_t* p = frag_ptr(0);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            buf[i] = ldg16(p + 32 * i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    uint32_t L[KCAP];
+#pragma unroll
+    for (int e = 0; e < KCAP; ++e) L[e] = 0u;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* hrow = lds + j * pitch + 8 * g;  // B fragment of lane (j, g): hidden row j
+    for (int b = 0; b < nblk; ++b) {
+        const int tw = b / nKB;
+        const int kb = (b - tw * nKB) * PF;
+        const uint16_t* pn = frag_ptr(b + 1);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const bf16x8 hb = as_bf16x8(*reinterpret_cast<const u32x4*>(hrow + (kb + i) * 32));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf[i]), hb, acc, 0, 0, 0);
+            buf[i] = ldg16(pn + 32 * i);
+        }
+        if (kb + PF == nK) {
+            // the tile is done: key its logits of row j and keep the best
+            const int vt = (t0 + wave + SK_WAVES * tw) * 16 + 4 * g;
+            if (j < T) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = vt + e;
+                    if (v < V) {
+                        const uint32_t p = (order_key(logit_key_bits(acc[e], s, c, inv_c)) << 16) |
+                                           (0xffffu - (uint32_t)(v - v0));
+                        if (p > L[KCAP - 1]) list_insert<KCAP>(L, p);
+                    }
+                }
+            }
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // the 32 lists of each row -> LDS (over the hidden rows), then a 32-lane
+    // merge per row: wave w takes rows w and w + 8 (lanes 0-31 and 32-63)
+    __syncthreads();
+    uint32_t* lists = reinterpret_cast<uint32_t*>(lds);
+    {
+        uint32_t* dst = lists + ((j * 32) + wave * 4 + g) * KCAP;
+#pragma unroll
+        for (int e = 0; e < KCAP; ++e) dst[e] = L[e];
+    }
+    __syncthreads();
+    const int row = wave + 8 * (lane >> 5);
+    const int sub = lane & 31;
+    {
+        const uint32_t* src = lists + (row * 32 + sub) * KCAP;
+#pragma unroll
+        for (int e = 0; e < KCAP; ++e) L[e] = src[e];
+    }
+    if (row >= T) return;
+    uint64_t* out = part + ((int64_t)row * G + grp) * KCAP;
+    for (int r = 0; r < KCAP; ++r) {
+        uint32_t best = L[0];
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) best = max(best, (uint32_t)__shfl_xor((int)best, off, 32));
+        if (best != 0u && L[0] == best) {  // keys of one group differ in the column bits: one owner
+#pragma unroll
+            for (int e = 0; e < KCAP - 1; ++e) L[e] = L[e + 1];
+            L[KCAP - 1] = 0u;
+        }
+        if (sub == 0) {
+            uint64_t e = 0;
+            if (best != 0u) {
+                const uint32_t id = (uint32_t)v0 + (0xffffu - (best & 0xffffu));
+                e = ((uint64_t)(best >> 16) << 32) | (uint64_t)(~id);
+            }
+            out[r] = e;
+        }
+    }
+}
+
 struct LmPlan {
     int BM, BN, KCAP, nM, nN, G, xmx;
     int64_t nwg;
     size_t ws;
+    int skinny_pf;  // > 0: lm_topk_skinny with this many fragments in flight per lane
 };
 
-static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p) {
-    (void)Hd;
+// allow_skinny: the streaming kernel may be used (not with the rank projection
+// riding along, which the tile kernel carries).
+static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p, bool allow_skinny = true) {
     p.KCAP = k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
+    p.skinny_pf = 0;
+    if (allow_skinny && T <= 16 && Hd <= SK_MAXHD && Hd % 128 == 0) {
+        // up to 16 rows: one workgroup per CU streams a run of 16-row vocabulary tiles
+        const int nK = (int)(Hd / 32);
+        p.skinny_pf = nK % 16 == 0 ? 16 : nK % 8 == 0 ? 8 : 4;
+        const int64_t ntiles = (V + 15) / 16;
+        int64_t G = ntiles < 256 ? ntiles : 256;
+        while (((ntiles + G - 1) / G) * 16 > 65536) ++G;
+        p.BM = 16;
+        p.BN = 16;
+        p.nM = 1;
+        p.nN = (int)ntiles;
+        p.G = (int)G;
+        p.nwg = G;
+        p.xmx = 0;
+        const size_t lists = (size_t)T * (size_t)p.G * (size_t)p.KCAP * sizeof(uint64_t);
+        const size_t level = p.G > 16 ? (size_t)T * (size_t)((p.G + 15) / 16) * (size_t)p.KCAP * sizeof(uint64_t) : 0;
+        p.ws = lists + 2 * level;
+        return true;
+    }
     // Up to 64 rows the contraction is far from dense: 64-row tiles do a quarter
     // of a 256-row tile's MFMA work for the same weight stream, and 128-column
     // tiles spread the vocabulary over more workgroups.
@@ -643,7 +811,16 @@ template <int KCAP>
 static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, int T, int V, int Hd, int k,
                        float s, float c, uint64_t* part, int32_t* ids, float* logits, const LmProj& pj,
                        hipStream_t st) {
-    if (p.BM == 64)
+    if (p.skinny_pf > 0) {
+        const float inv_c = c > 0.f ? 1.0f / c : 0.f;
+        const dim3 grid((unsigned)p.nwg), block(SK_THREADS);
+        if (p.skinny_pf == 16)
+            hipLaunchKernelGGL((lm_topk_skinny<KCAP, 16>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
+        else if (p.skinny_pf == 8)
+            hipLaunchKernelGGL((lm_topk_skinny<KCAP, 8>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
+        else
+            hipLaunchKernelGGL((lm_topk_skinny<KCAP, 4>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
+    } else if (p.BM == 64)
         launch_tiles<64, 128, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
     else if (p.BN == 256)
         launch_tiles<LM_BM, 256, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
@@ -673,15 +850,18 @@ static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, in
 using namespace dflash;
 
 extern "C" size_t dflash_lm_topk_workspace_size(int64_t T, int64_t V, int64_t Hd, int32_t k) {
-    LmPlan p;
-    if (T < 1 || V < 1 || Hd < 1 || k < 1 || k > 64 || !lm_plan(T, V, Hd, k, p)) return 0;
-    return p.ws;
+    LmPlan p, q;
+    if (T < 1 || V < 1 || Hd < 1 || k < 1 || k > 64 || !lm_plan(T, V, Hd, k, p) || !lm_plan(T, V, Hd, k, q, false))
+        return 0;
+    // enough for either kernel (dflash_lm_topk_proj never takes the streaming one)
+    return p.ws > q.ws ? p.ws : q.ws;
 }
 
 // Host checks of the arguments every LM-head call shares (no HIP call); fills
 // the launch plan.
 static int lm_topk_validate(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd, int32_t k,
-                            float output_multiplier, float softcap, int32_t* ids, float* logits, LmPlan& p) {
+                            float output_multiplier, float softcap, int32_t* ids, float* logits, LmPlan& p,
+                            bool allow_skinny) {
     if (!H || !W || !ids || !logits) return DFLASH_ERR_INVALID_ARG;
     if (!DFLASH_ALIGNED16(H) || !DFLASH_ALIGNED16(W)) return DFLASH_ERR_INVALID_ARG;
     if (T < 1 || V < 1 || Hd < 1 || k < 1 || k > V) return DFLASH_ERR_INVALID_ARG;
@@ -691,7 +871,7 @@ static int lm_topk_validate(const uint16_t* H, const uint16_t* W, int64_t T, int
     if (T > INT32_MAX || V > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     // tile buffer ranges and lane offsets (up to 256 rows of Hd bf16) are int32 byte counts
     if ((int64_t)256 * Hd * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
-    if (!lm_plan(T, V, Hd, k, p)) return DFLASH_ERR_UNSUPPORTED;
+    if (!lm_plan(T, V, Hd, k, p, allow_skinny)) return DFLASH_ERR_UNSUPPORTED;
     return DFLASH_OK;
 }
 
@@ -718,7 +898,7 @@ static int lm_topk_common(const uint16_t* H, const uint16_t* W, int64_t T, int64
                           size_t ws_bytes, const LmProj& pj, void* stream) {
     if (!ws || !DFLASH_ALIGNED16(ws)) return DFLASH_ERR_INVALID_ARG;
     LmPlan p;
-    const int st = lm_topk_validate(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, p);
+    const int st = lm_topk_validate(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, p, pj.Wp == nullptr);
     if (st != DFLASH_OK) return st;
     if (ws_bytes < p.ws) return DFLASH_ERR_WORKSPACE;
     return lm_topk_launch(p, H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, ws, pj, stream);
@@ -785,7 +965,7 @@ extern "C" int dflash_lm_topk_noalloc(const uint16_t* H, const uint16_t* W, int6
                                       int32_t k, float output_multiplier, float softcap, int32_t* ids,
                                       float* logits, void* stream) {
     LmPlan p;
-    int st = lm_topk_validate(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, p);
+    int st = lm_topk_validate(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, p, true);
     if (st != DFLASH_OK) return st;
     if (p.ws > DFLASH_LM_TOPK_SCRATCH_BYTES) return DFLASH_ERR_SCRATCH;
     void* ws = nullptr;

@@ -134,9 +134,23 @@ def _full_rows_vs_golden(B, d, r0, T, label):
 
 @pytest.mark.parametrize("T", [16, 33, 64])
 def test_skinny_rows_full_vocab(B, full_inputs, T):
-    """Up to 64 rows the head runs 64-row tiles: every row of the full
-    vocabulary's product against the oracle, 16 / 33 (a ragged tile) / 64."""
+    """Up to 16 rows the head streams W (the bandwidth regime), up to 64 it runs
+    64-row tiles: every row of the full vocabulary's product against the
+    oracle's goldens, 16 / 33 (a ragged tile) / 64."""
     _full_rows_vs_golden(B, full_inputs, (T * 37) % 1000, T, f"skinny T{T}")
+
+
+@pytest.mark.parametrize("T,V,Hd,k,s,c", [
+    # up to 16 rows with Hd % 128 == 0, Hd <= 4096: the streaming kernel
+    (1, 777, 128, 1, 1.0, 0.0),        # one row, 4 fragments in flight, a ragged last tile
+    (5, 4099, 256, 8, 0.75, 20.0),     # 8 fragments in flight
+    (16, 20000, 384, 64, 0.5, 30.0),   # K steps not a multiple of 8, k = 64
+    (13, 1000, 4096, 16, 2.0, 5.0),    # fewer tiles than CUs, 16 fragments in flight
+    (16, 70001, 1024, 32, 1.0, 30.0),  # k = 32, two merge levels
+])
+def test_streaming_rows(B, T, V, Hd, k, s, c):
+    H, W = _random_case(T * 31 + V + Hd, T, V, Hd, 0.1)
+    _check(B, H, W, k, s, c, label=f"streaming T{T} V{V} Hd{Hd} k{k}")
 
 
 @pytest.mark.parametrize("T,V,Hd,k", [
