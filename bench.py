@@ -510,7 +510,7 @@ def main():
                   "softcap 30"),
                  ("lm_topk_full_vocab_16_rows", H[:16].contiguous(), W, k, cand["multiplier"], cand["softcap"],
                   "16 rows (one request's 16 steps), vocab 151936, hidden 4096, top_k 16, multiplier 0.5, "
-                  "softcap 30; 64-row tiles")]
+                  "softcap 30; the streaming kernel")]
         for name, Hx, Wx, kx, sx, cx, desc in cases:
             Tx, Hdx = Hx.shape
             Vx = Wx.shape[0]
