@@ -638,7 +638,7 @@ __global__ __launch_bounds__(SK_THREADS) void lm_topk_skinny(const uint16_t* __r
         const uint16_t* p = frag_ptr(0);
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            buf[i] = ldg16(p + 32 * i);
+            buf[i] = ldg16_stream(p + 32 * i);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(SK_THREADS) void lm_topk_skinny(const uint16_t* __r
         for (int i = 0; i < PF; ++i) {
             const bf16x8 hb = as_bf16x8(*reinterpret_cast<const u32x4*>(hrow + (kb + i) * 32));
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf[i]), hb, acc, 0, 0, 0);
-            buf[i] = ldg16(pn + 32 * i);
+            buf[i] = ldg16_stream(pn + 32 * i);
         }
         if (kb + PF == nK) {
             // the tile is done: key its logits of row j and keep the best
