@@ -94,16 +94,16 @@ __device__ __forceinline__ void dma_offsets(int (&voff)[NI], int& lcpack, int wa
 }
 
 // One of those loads (instruction j of this wave) for the slice starting at
-// column k0; see dma_slice.
-template <int NI, bool TAIL>
+// column k0; see dma_slice.  AUX is the load's cache policy (2: nontemporal).
+template <int NI, bool TAIL, int AUX = 0>
 __device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, const int* voff,
                                         int lcpack, int wave_s, int Hd, int k0, int j) {
     auto* dst = (__attribute__((address_space(3))) void*)(lds_tile + (wave_s * NI + j) * 512);
     if (TAIL) {
         const bool in = k0 + ((lcpack >> (3 * j)) & 7) * 8 < Hd;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, in ? voff[j] + k0 * 2 : (int)0x80000000, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, in ? voff[j] + k0 * 2 : (int)0x80000000, 0, 0, AUX);
     } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff[j], k0 * 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff[j], k0 * 2, 0, AUX);
     }
 }
 
@@ -112,11 +112,11 @@ __device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t rsrc, uint16_t* l
 // column offset goes into the scalar offset and no vector work is needed; with
 // one, chunks past Hd get an out-of-range offset.  Branch-free, so the loads
 // can be interleaved with MFMAs by the scheduler.
-template <int NI, bool TAIL>
+template <int NI, bool TAIL, int AUX = 0>
 __device__ __forceinline__ void dma_slice(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_tile, const int* voff,
                                           int lcpack, int wave_s, int Hd, int k0) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) dma_one<NI, TAIL>(rsrc, lds_tile, voff, lcpack, wave_s, Hd, k0, j);
+    for (int j = 0; j < NI; ++j) dma_one<NI, TAIL, AUX>(rsrc, lds_tile, voff, lcpack, wave_s, Hd, k0, j);
 }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }

@@ -119,7 +119,7 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
     L[0] = max(L[0], p);
 }
 
-template <int BM, int BN, int KCAP, bool TAIL>
+template <int BM, int BN, int KCAP, bool TAIL, bool WNT>
 __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ W, int T, int V, int Hd,
     int nM, int nN, int G, int xmx, float s, float c, float inv_c,
@@ -136,6 +136,12 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
     constexpr int SP = QCOLS + 4;            // row pitch (floats) of the epilogue staging
     constexpr int SMEM = (NSLOT * UNIT > BM * SP * 2) ? NSLOT * UNIT : BM * SP * 2;
     static_assert(BM == 256 || BM == 64, "row tile");
+    // WNT: the weight's LDS-DMA loads carry the nontemporal hint.  It is set when
+    // one row tile covers every row, so that each W tile is read by one
+    // workgroup only; the hint then lets the weight stream run closer to the HBM
+    // peak.  With several row tiles the workgroups of an XCD share W tiles
+    // through L2, and the hint would cost those hits.
+    constexpr int WAUX = WNT ? 2 : 0;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
     float* stage = reinterpret_cast<float*>(smem);
 
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                 if (dma == 1 && q < NIA)
                     dma_one<NIA, TAIL>(rsA, smem + dslot * UNIT, voffA, lcA, wave_s, hd_t, dkt * LM_BK, q);
                 if (dma == 2 && q < NIB)
-                    dma_one<NIB, TAIL>(rsB, smem + dslot * UNIT, voffB, lcB, wave_s, hd_t, dkt * LM_BK, q);
+                    dma_one<NIB, TAIL, WAUX>(rsB, smem + dslot * UNIT, voffB, lcB, wave_s, hd_t, dkt * LM_BK, q);
             }
             mfmas(fa, fb);
 #pragma unroll
@@ -286,9 +292,9 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
         // an A half (the hidden states, L2/MALL resident) for one.  The wait
         // before each barrier lets exactly the newest B half stay in flight.
         bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
-        dma_slice<NIB, TAIL>(rsB, smem + 0 * UNIT, voffB, lcB, wave_s, hd_t, 0);
+        dma_slice<NIB, TAIL, WAUX>(rsB, smem + 0 * UNIT, voffB, lcB, wave_s, hd_t, 0);
         dma_slice<NIA, TAIL>(rsA, smem + 1 * UNIT, voffA, lcA, wave_s, hd_t, 0);
-        dma_slice<NIB, TAIL>(rsB, smem + 2 * UNIT, voffB, lcB, wave_s, hd_t, LM_BK);  // past K: zeros, unused
+        dma_slice<NIB, TAIL, WAUX>(rsB, smem + 2 * UNIT, voffB, lcB, wave_s, hd_t, LM_BK);  // past K: zeros, unused
         dma_slice<NIA, TAIL>(rsA, smem + 3 * UNIT, voffA, lcA, wave_s, hd_t, LM_BK);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(NIB + NIA));  // slice 0 landed
         __builtin_amdgcn_s_barrier();
@@ -799,12 +805,15 @@ template <int BM, int BN, int KCAP>
 static void launch_tiles(const LmPlan& p, const uint16_t* H, const uint16_t* W, int T, int V, int Hd,
                          float s, float c, uint64_t* part, const LmProj& pj, hipStream_t st) {
     const float inv_c = c > 0.f ? 1.0f / c : 0.f;
-    if (Hd % LM_BK == 0)
-        hipLaunchKernelGGL((lm_topk_tiles<BM, BN, KCAP, false>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H,
-                           W, T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
+    if (Hd % LM_BK == 0 && p.nM == 1)
+        hipLaunchKernelGGL((lm_topk_tiles<BM, BN, KCAP, false, true>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st,
+                           H, W, T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
+    else if (Hd % LM_BK == 0)
+        hipLaunchKernelGGL((lm_topk_tiles<BM, BN, KCAP, false, false>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0,
+                           st, H, W, T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
     else
-        hipLaunchKernelGGL((lm_topk_tiles<BM, BN, KCAP, true>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st, H,
-                           W, T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
+        hipLaunchKernelGGL((lm_topk_tiles<BM, BN, KCAP, true, false>), dim3((unsigned)p.nwg), dim3(LM_THREADS), 0, st,
+                           H, W, T, V, Hd, p.nM, p.nN, p.G, p.xmx, s, c, inv_c, part, pj.Wp, pj.R, pj.hp);
 }
 
 template <int KCAP>
