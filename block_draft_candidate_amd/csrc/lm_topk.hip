@@ -909,7 +909,8 @@ static int lm_topk_common(const uint16_t* H, const uint16_t* W, int64_t T, int64
     LmPlan p;
     const int st = lm_topk_validate(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, p, pj.Wp == nullptr);
     if (st != DFLASH_OK) return st;
-    if (ws_bytes < p.ws) return DFLASH_ERR_WORKSPACE;
+    // the documented size (enough for either kernel), not just this call's plan
+    if (ws_bytes < dflash_lm_topk_workspace_size(T, V, Hd, k)) return DFLASH_ERR_WORKSPACE;
     return lm_topk_launch(p, H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, ws, pj, stream);
 }
 
@@ -976,7 +977,7 @@ extern "C" int dflash_lm_topk_noalloc(const uint16_t* H, const uint16_t* W, int6
     LmPlan p;
     int st = lm_topk_validate(H, W, T, V, Hd, k, output_multiplier, softcap, ids, logits, p, true);
     if (st != DFLASH_OK) return st;
-    if (p.ws > DFLASH_LM_TOPK_SCRATCH_BYTES) return DFLASH_ERR_SCRATCH;
+    if (dflash_lm_topk_workspace_size(T, V, Hd, k) > DFLASH_LM_TOPK_SCRATCH_BYTES) return DFLASH_ERR_SCRATCH;
     void* ws = nullptr;
     st = lm_scratch_address(&ws);
     if (st != DFLASH_OK) return st;
