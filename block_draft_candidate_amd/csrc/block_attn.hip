@@ -31,7 +31,7 @@
 //   * With an fp8 cache (E4M3fn or E5M2) the LDS-DMA brings the tile's
 //     256-byte fp8 rows into a ring of staging buffers instead, and after the
 //     tile's barrier the workgroup decodes them into one bf16 tile in the layout
-//     above (hardware fp8 -> fp32 conversions, exact, then the top halves);
+//     above (hardware fp8 -> bf16 conversions, exact);
 //     the rest is the bf16 path.  The layer's K scale is
 //     folded into the score scale and its V scale into the output.
 #include "fp8.h"
@@ -78,14 +78,17 @@ __device__ __forceinline__ void at_load_block_rows(const void* blk, int row_byte
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 2);
 }
 
-// Two fp8 codes (the low or high half of a word) -> two bf16 packed in a word:
-// v_cvt_pk_f32_fp8 / _bf8 give the OCP E4M3 / E5M2 values exactly as fp32, and
-// every finite one is a bf16 number, so the top halves are exact.
+// Two fp8 codes (the low or high half of a word) -> two bf16 packed in a word,
+// one v_cvt_scalef32_pk_bf16_fp8 / _bf8 with scale 1: every finite OCP E4M3 /
+// E5M2 value is a bf16 number, so the conversion is exact (checked on the
+// device over all 65536 code pairs of both formats and both halves against the
+// fp32 conversion's top halves: bit-identical, NaNs included).
+typedef __attribute__((ext_vector_type(2))) __bf16 at_bf16x2;
 template <int F8, bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-    const auto f = F8 == FP8_E4M3 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI)
-                                  : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
-    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+    const at_bf16x2 r = F8 == FP8_E4M3 ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI)
+                                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 template <int G, int F8>
