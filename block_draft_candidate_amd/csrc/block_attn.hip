@@ -29,10 +29,10 @@
 //     from an out-of-range offset and land as zeros: their weight is zero, and
 //     a stale NaN or Inf there must not reach the output through 0 * NaN.
 //   * With an fp8 cache (E4M3fn or E5M2) the LDS-DMA brings the tile's
-//     256-byte fp8 rows into a ring of staging buffers instead, and after the
-//     tile's barrier the workgroup decodes them into one bf16 tile in the layout
-//     above (hardware fp8 -> bf16 conversions, exact);
-//     the rest is the bf16 path.  The layer's K scale is
+//     256-byte fp8 rows into the ring instead (chunks swizzled by f8_swz), and
+//     each wave converts its MFMA operands in registers (K from 8-byte reads,
+//     V^T from the 8-bit transposing read; hardware fp8 -> bf16 conversions,
+//     exact); the rest is the bf16 path.  The layer's K scale is
 //     folded into the score scale and its V scale into the output.
 #include "fp8.h"
 
@@ -41,7 +41,7 @@ namespace dflash {
 constexpr int AT_D = 128;
 constexpr int AT_BS = 16;      // cache block size
 constexpr int AT_TK = 32;      // keys per tile
-constexpr int AT_NST = 2;      // LDS ring stages (tiles): 36 KB of LDS per workgroup lets four
+constexpr int AT_NST = 2;      // LDS ring stages (tiles): 36 KB of LDS per workgroup (bf16) lets four
                                // workgroups share a CU, which hides more than deeper rings with
                                // fewer workgroups (measured: 2 stages 194 us, 3: 256, 4: 251, 8: 409)
 constexpr int AT_BTCAP = 1024; // block-table entries staged in LDS (longer spans read it from HBM)
@@ -91,6 +91,13 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// fp8 tiles: row r keeps its 16-byte chunk c (K: 0-7, V: 8-15) at physical chunk
+// c ^ f8_swz(r).  The 16 rows a K fragment read spans, and the 8 keys a V
+// transpose read spans (4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3), all get
+// different values, so neither read has bank conflicts.
+__device__ __forceinline__ int f8_swz(int r) { return (r & 15) ^ (((r >> 4) & 1) << 2); }
+typedef __attribute__((ext_vector_type(2))) int at_v2i;
+
 template <int G, int F8>
 __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ cache, int64_t num_blocks,
@@ -100,13 +107,12 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     constexpr int NI = F8 == FP8_NONE ? AT_TK / 2 / G : AT_TK / 4 / G;
     constexpr int RB = F8 == FP8_NONE ? AT_ROW * 2 : AT_ROW;  // bytes per cache row
     static_assert(NI >= 1, "at least one LDS-DMA instruction per wave");
-    // bf16: a ring of AT_NST tiles; fp8: one bf16 tile, then a ring of AT_NST
-    // fp8 tiles (the same bytes); then the staged block-table entries
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[AT_NST * AT_TK * AT_ROW + AT_BTCAP * 2];
-    int32_t* const btl = reinterpret_cast<int32_t*>(smem + AT_NST * AT_TK * AT_ROW);
-    static_assert(F8 == FP8_NONE || AT_NST * AT_TK * AT_ROW <= (AT_NST * AT_TK * AT_ROW * 2 - AT_TK * AT_ROW * 2),
-                  "fp8 ring and bf16 tile fit the bf16 ring");
-    uint8_t* const ring8 = reinterpret_cast<uint8_t*>(smem + AT_TK * AT_ROW);
+    // a ring of AT_NST tiles (bf16 rows, or fp8 rows at half the bytes), then
+    // the staged block-table entries
+    constexpr int RING = AT_NST * AT_TK * RB / 2;  // elements of uint16_t
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[RING + AT_BTCAP * 2];
+    int32_t* const btl = reinterpret_cast<int32_t*>(smem + RING);
+    uint8_t* const ring8 = reinterpret_cast<uint8_t*>(smem);
     if (F8 != FP8_NONE) scale_log2 *= kv_scale[0];
 
     const int r = blockIdx.x / Hkv;
@@ -154,7 +160,8 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
     // 2q + i/32, physical 16-byte chunk i % 32 of the 512-byte row.  Physical
     // chunk pc < 16 holds K chunk pc ^ (row % 16); pc >= 16 holds V chunk
     // (pc - 16) ^ (2 (row % 8)).  (fp8: instruction covers rows 4q .. 4q+3, lane
-    // i -> row 4q + i/16, chunk i % 16 of the 256-byte row, unswizzled.)
+    // i -> row 4q + i/16, physical 16-byte chunk i % 16 of the 256-byte row,
+    // holding K | V chunk i % 16 ^ f8_swz(row).)
     // Per-lane byte offsets inside a cache block (tile-independent), and per
     // tile one scalar block base per instruction.
     int loff[NI];
@@ -166,8 +173,8 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
             const int lchunk = pc < 16 ? (pc ^ rr) : (16 + ((pc - 16) ^ (2 * (rr & 7))));
             loff[j] = (rr * AT_ROW + lchunk * 8) * 2;
         } else {
-            const int rr = (4 * (wave_s * NI + j) + (lane >> 4)) & 15;
-            loff[j] = rr * AT_ROW + (lane & 15) * 16;
+            const int trow = 4 * (wave_s * NI + j) + (lane >> 4);  // tile row
+            loff[j] = (trow & 15) * AT_ROW + (((lane & 15) ^ f8_swz(trow)) * 16);
         }
     }
     constexpr int RPI = F8 == FP8_NONE ? 2 : 4;  // tile rows per DMA instruction
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
             const int b = __builtin_amdgcn_readfirstlane(block_of(kb / AT_BS + (RPI * qd) / AT_BS));
             const uint8_t* blk = reinterpret_cast<const uint8_t*>(cache) + ((int64_t)b * Hkv + hk) * AT_BS * RB;
             void* dst = F8 == FP8_NONE ? (void*)(smem + st * AT_TK * AT_ROW + qd * 512)
-                                       : (void*)(ring8 + st * AT_TK * AT_ROW + qd * 1024);
+                                       : (void*)(ring8 + st * AT_TK * AT_ROW + qd * 1024);  // (fp8 rows: AT_ROW bytes)
             // rows at or past the request's length read as zeros (offset past the range)
             at_load_block_rows(blk, RB, kb + RPI * qd + lrow < L ? loff[j] : (int)0x80000000, dst);
         }
@@ -203,31 +210,8 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
         __builtin_amdgcn_s_barrier();  // ... and every wave's; the stage of tile - 1 is free
         at_fence();
         if (tile + AT_NST - 1 < ntiles) issue(tile + AT_NST - 1, (tile + AT_NST - 1) % AT_NST);
-        if (F8 != FP8_NONE) {
-            // decode the fp8 tile into the bf16 tile (16 codes -> two swizzled
-            // 16-byte chunks per step); the bf16 tile's readers of the previous
-            // tile are past the barrier above
-            const uint8_t* src = ring8 + st * AT_TK * AT_ROW;
-            for (int c = tid; c < AT_TK * 16; c += 64 * G) {
-                const int row = c >> 4, u = c & 15;
-                const u32x4 w = *reinterpret_cast<const u32x4*>(src + row * AT_ROW + u * 16);
-                u32x4 h[2];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h[j >> 1][2 * (j & 1)] = fp8x2_to_bf16x2<F8, false>(w[j]);
-                    h[j >> 1][2 * (j & 1) + 1] = fp8x2_to_bf16x2<F8, true>(w[j]);
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int pch = u < 8 ? ((2 * u + hh) ^ (row & 15)) : (16 + ((2 * (u - 8) + hh) ^ (2 * (row & 7))));
-                    *reinterpret_cast<u32x4*>(smem + row * AT_ROW + pch * 8) = h[hh];
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-            __builtin_amdgcn_s_barrier();
-            at_fence();
-        }
-        const uint16_t* tb = F8 == FP8_NONE ? smem + st * AT_TK * AT_ROW : smem;
+        const uint16_t* tb = smem + st * AT_TK * AT_ROW;   // bf16 tile
+        const uint8_t* t8 = ring8 + st * AT_TK * AT_ROW;     // fp8 tile (AT_ROW bytes per row)
         const int kb = kstart + tile * AT_TK;
         // every key of the tile is visible to every query of the block (the
         // highest window start is L - window, for the last query), and every
@@ -244,8 +228,18 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
             const int row = kblk * 16 + qi;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int ch = (4 * s + g) ^ (row & 15);
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(tb + row * AT_ROW + ch * 8));
+                bf16x8 kf;
+                if (F8 == FP8_NONE) {
+                    const int ch = (4 * s + g) ^ (row & 15);
+                    kf = as_bf16x8(*reinterpret_cast<const u32x4*>(tb + row * AT_ROW + ch * 8));
+                } else {
+                    // 8 codes: half (g & 1) of the row's K chunk 2 s + g / 2
+                    const int u = 4 * s + g;
+                    const u32x2 w = *reinterpret_cast<const u32x2*>(t8 + row * AT_ROW +
+                                                                    (((u >> 1) ^ f8_swz(row)) * 16) + (u & 1) * 8);
+                    kf = as_bf16x8(u32x4{fp8x2_to_bf16x2<F8, false>(w[0]), fp8x2_to_bf16x2<F8, true>(w[0]),
+                                         fp8x2_to_bf16x2<F8, false>(w[1]), fp8x2_to_bf16x2<F8, true>(w[1])});
+                }
                 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc, 0, 0, 0);
             }
             if (interior) {
@@ -302,18 +296,35 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(
             const bf16x8 pfl = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
             const int r1 = 32 * s2 + 4 * g + (p >> 2);
             const int r2 = r1 + 16;
+            // fp8: ds_read_b64_tr_b8 gives lane 8 h + j of a 16-lane group byte j
+            // of the 8 bytes read by the group's lanes h, h + 2, .., h + 14 (element
+            // e from lane 2 e + h).  So lane 2 e + h of group g reads key e of the
+            // group's MFMA K order (32 s2 + 4 g + e, then 32 s2 + 16 + 4 g + e - 4)
+            // at V bytes 16 mb + 8 h .. + 8: lane (p, g) then holds d = 16 mb + p
+            // for those 8 keys.
+            const int e8 = p >> 1;
+            const int rk = 32 * s2 + (e8 < 4 ? 4 * g + e8 : 16 + 4 * g + (e8 - 4));
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
-                // 8-byte chunk of d = 16 mb + 4 (p % 4) in the V half, swizzled by row
-                const int c8 = 4 * mb + (p & 3);
-                const int o1 = r1 * AT_ROW + AT_D + ((c8 ^ (4 * (r1 & 7))) << 2);
-                const int o2 = r2 * AT_ROW + AT_D + ((c8 ^ (4 * (r2 & 7))) << 2);
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4*)(tb + o1));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4*)(tb + o2));
-                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-                const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                u32x4 vv;
+                if (F8 == FP8_NONE) {
+                    // 8-byte chunk of d = 16 mb + 4 (p % 4) in the V half, swizzled by row
+                    const int c8 = 4 * mb + (p & 3);
+                    const int o1 = r1 * AT_ROW + AT_D + ((c8 ^ (4 * (r1 & 7))) << 2);
+                    const int o2 = r2 * AT_ROW + AT_D + ((c8 ^ (4 * (r2 & 7))) << 2);
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)(tb + o1));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)(tb + o2));
+                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+                    vv = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+                } else {
+                    const int o = rk * AT_ROW + (((8 + mb) ^ f8_swz(rk)) * 16) + (p & 1) * 8;
+                    const u32x2 w = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) at_v2i*)(t8 + o)));
+                    vv = u32x4{fp8x2_to_bf16x2<F8, false>(w[0]), fp8x2_to_bf16x2<F8, true>(w[0]),
+                               fp8x2_to_bf16x2<F8, false>(w[1]), fp8x2_to_bf16x2<F8, true>(w[1])};
+                }
                 o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), pfl, o[mb], 0, 0, 0);
                 o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), pfh, o[mb], 0, 0, 0);
             }
