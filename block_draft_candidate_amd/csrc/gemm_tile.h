@@ -44,7 +44,7 @@ __device__ __forceinline__ void gemm_tile_mainloop(uint16_t* smem, __amdgpu_buff
     constexpr int NIB = BN / 8 / 4;          // (B)
     constexpr int UNIT = GT_UNIT;
     constexpr int NSLOT = GT_NSLOT;
-    static_assert(BN == 128 || BN == 256, "tile width");
+    static_assert(BN == 128 || BN == 192 || BN == 256, "tile width");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -144,22 +144,29 @@ __device__ __forceinline__ void gemm_tile_mainloop(uint16_t* smem, __amdgpu_buff
     compiler_fence();
 }
 
-// Stage the tile's 128-column group `pass` (columns 128 * pass ..) row-major
-// into `stage` (pitch GT_SP floats) from the waves that hold it, then wait for
-// the whole workgroup.  In the 32x32 MFMA layout lane l holds column l % 32 and
-// rows 8b + 4(l / 32) + e, e = 0..3; the writes go straight from the
-// accumulator registers.
+// Column groups of a staged pass: 128 columns, or (BN = 192) one wave
+// column's 96.
+template <int BN>
+constexpr int gemm_tile_group() { return BN % 128 == 0 ? 128 : BN / 2; }
+
+// Stage the tile's column group `pass` (columns GW * pass .., GW =
+// gemm_tile_group<BN>()) row-major into `stage` (pitch GT_SP floats) from the
+// waves that hold it, then wait for the whole workgroup.  In the 32x32 MFMA
+// layout lane l holds column l % 32 and rows 8b + 4(l / 32) + e, e = 0..3; the
+// writes go straight from the accumulator registers.
 template <int BN>
 __device__ __forceinline__ void gemm_tile_stage(float* stage, const f32x16 (&acc)[4][BN / 64], int pass) {
     constexpr int WN = BN / 2, NB = WN / 32, MB = 4;
+    constexpr int GW = gemm_tile_group<BN>();
+    static_assert(GW + 4 <= GT_SP, "a group fits the staging pitch");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int fr = lane & 31;
-    if ((wn * WN) / 128 == pass) {
+    if ((wn * WN) / GW == pass) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const int col = (wn * WN) % 128 + j * 32 + fr;
+            const int col = (wn * WN) % GW + j * 32 + fr;
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -189,9 +196,10 @@ __device__ __forceinline__ void gemm_tile_pass_done() {
 }
 
 // Tile width for a launch of 256 x BN tiles over rows x cols outputs, one tile
-// per CU at a time: 256 or 128, whichever needs fewer width-weighted rounds
-// of the device's compute units (ties: 256).
-static inline int gemm_tile_width(int64_t rows, int64_t cols) {
+// per CU at a time: 256, 192 (only where the epilogue takes 96-column groups,
+// allow192) or 128, whichever needs the fewest width-weighted rounds of the
+// device's compute units (ties: the wider).
+static inline int gemm_tile_width(int64_t rows, int64_t cols, bool allow192 = false) {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
@@ -199,7 +207,10 @@ static inline int gemm_tile_width(int64_t rows, int64_t cols) {
     }
     const int64_t nM = (rows + GT_BM - 1) / GT_BM;
     auto cost = [&](int64_t bn) { return ((nM * ((cols + bn - 1) / bn) + ncu - 1) / ncu) * bn; };
-    return cost(128) < cost(256) ? 128 : 256;
+    int best = 256;
+    if (allow192 && cost(192) < cost(best)) best = 192;
+    if (cost(128) < cost(best)) best = 128;
+    return best;
 }
 
 // Tile q of the launch: workgroup ids go to the 8 XCDs round-robin, and XCD x

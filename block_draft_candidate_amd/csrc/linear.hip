@@ -2,10 +2,11 @@
 // projections around its attention (DFlash2BeamAttention: qkv_proj before the
 // fused q/k norm + RoPE + cache write, o_proj after the attention).
 //
-// The 256 x BN tile of gemm_tile.h; the epilogue stages each 128-column group
-// of the tile row-major in LDS, and thread t rounds row t's fp32 sums once to
-// bf16 and stores them with 16-byte writes.  Columns past N are computed on
-// zero rows of W and never stored.
+// The 256 x BN tile of gemm_tile.h (BN = 256, 192 or 128, whichever fills the
+// CUs in the fewest width-weighted rounds); the epilogue stages each column
+// group of the tile (128 columns, or 96 at BN = 192) row-major in LDS, and
+// thread t rounds row t's fp32 sums once to bf16 and stores them with 16-byte
+// writes.  Columns past N are computed on zero rows of W and never stored.
 #include "gemm_tile.h"
 
 namespace dflash {
@@ -29,15 +30,16 @@ __global__ __launch_bounds__(GT_THREADS, 1) void linear_tiles(const uint16_t* __
     f32x16 acc[4][BN / 64];
     gemm_tile_mainloop<BN, TAIL>(smem, rsA, rsB, K, acc);
 
+    constexpr int GW = gemm_tile_group<BN>();
 #pragma unroll
-    for (int pass = 0; pass < BN / 128; ++pass) {
-        const int c0 = n0 + pass * 128;
+    for (int pass = 0; pass < BN / GW; ++pass) {
+        const int c0 = n0 + pass * GW;
         if (c0 >= N) break;  // uniform: the tile's last groups past N
         gemm_tile_stage<BN>(stage, acc, pass);
         if (my_row < M) {
             const float* rowp = stage + threadIdx.x * GT_SP;
             uint16_t* dst = Y + (int64_t)my_row * ldy + c0;
-            const int nch = min(128, N - c0) / 8;  // N % 8 == 0
+            const int nch = min(GW, N - c0) / 8;  // N % 8 == 0
 #pragma unroll 4
             for (int c = 0; c < nch; ++c) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(rowp + 8 * c);
@@ -61,7 +63,7 @@ extern "C" int dflash_linear(const uint16_t* X, const uint16_t* W, int64_t M, in
     if (M < 1 || N < 1 || K < 1 || ldy < N) return DFLASH_ERR_INVALID_ARG;
     if (N % 8 != 0 || K % 8 != 0 || ldy % 8 != 0) return DFLASH_ERR_UNSUPPORTED;
     if (M > INT32_MAX || N > INT32_MAX || (int64_t)GT_BM * K * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
-    const int BN = gemm_tile_width(M, N);
+    const int BN = gemm_tile_width(M, N, true);
     const int nM = (int)((M + GT_BM - 1) / GT_BM);
     const int64_t ntiles = (int64_t)nM * ((N + BN - 1) / BN);
     if (ntiles > (int64_t)1 << 28) return DFLASH_ERR_UNSUPPORTED;
@@ -75,6 +77,9 @@ extern "C" int dflash_linear(const uint16_t* X, const uint16_t* W, int64_t M, in
     if (BN == 256) {
         if (tail) LIN_LAUNCH(256, true);
         else LIN_LAUNCH(256, false);
+    } else if (BN == 192) {
+        if (tail) LIN_LAUNCH(192, true);
+        else LIN_LAUNCH(192, false);
     } else {
         if (tail) LIN_LAUNCH(128, true);
         else LIN_LAUNCH(128, false);

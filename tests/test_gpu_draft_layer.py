@@ -27,7 +27,10 @@ def _bf(rng, shape, s=1.0):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 200, 328), (1, 8, 8), (513, 1024, 4096), (2048, 6144, 4096),
-                                   (2048, 4096, 4096)])
+                                   (2048, 4096, 4096),
+                                   # 192-wide tiles with a ragged last row tile, a ragged last
+                                   # column tile and a K tail
+                                   (2000, 6104, 200)])
 def test_linear(B, M, N, K):
     import torch
     from tests.gpu_common import dev_bf16, host_bf16, say
