@@ -8,8 +8,9 @@
 // G heads that share a kv head read each K/V tile from HBM once.  A wave's 16
 // MFMA columns are the block's (up to 16) queries.
 //   * K/V tiles of 32 keys (2 cache blocks) go straight from HBM to LDS with
-//     LDS-DMA (buffer_load_dwordx4 ... lds), whole 512-byte cache rows (K | V),
-//     in a ring of AT_NST stages (AT_NST - 1 tiles in flight).  K chunks are
+//     LDS-DMA (buffer_load_dwordx4 ... lds, nontemporal: each block is read
+//     once), whole 512-byte cache rows (K | V), in a ring of AT_NST stages
+//     (AT_NST - 1 tiles in flight).  K chunks are
 //     XOR-swizzled by row (16-byte units), V chunks by row (16-byte units,
 //     2 * (row % 8)), so both reads below are bank-conflict free.  The visible
 //     part of the request's block table is copied to LDS once, so issuing a
