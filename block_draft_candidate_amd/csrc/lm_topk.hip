@@ -23,8 +23,9 @@
 //   * Row slices and groups are blocked per XCD (workgroup ids go to XCDs
 //     round-robin), so each XCD's L2 serves W tiles to several row slices and
 //     H slices to several groups.
-//   * A merge kernel picks the k best of the groups' partial lists per row
-//     (with more than 16 groups, after levels that merge blocks of 16 lists).
+//   * A merge kernel picks the k best of the groups' partial lists per row:
+//     16 lanes per row up to 16 groups, a workgroup per row up to 256 groups
+//     (beyond that, after launches that merge blocks of 16 lists).
 #include <atomic>
 #include <mutex>
 
@@ -117,6 +118,26 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
 #pragma unroll
     for (int j = N - 1; j > 0; --j) L[j] = med3_u32(L[j], L[j - 1], p);
     L[0] = max(L[0], p);
+}
+
+// Bitonic sort of N (a power of two) values in registers, descending if DESC.
+template <int N, bool DESC>
+__device__ __forceinline__ void bitonic_sort(float (&a)[N]) {
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    // blocks of `size` alternate direction; the last stage (size N) is one block
+                    const bool asc = ((i & size) == 0) != DESC;
+                    const float lo = fminf(a[i], a[j]), hi = fmaxf(a[i], a[j]);
+                    a[i] = asc ? lo : hi;
+                    a[j] = asc ? hi : lo;
+                }
+            }
 }
 
 template <int BM, int BN, int KCAP, bool TAIL, bool WNT>
@@ -383,21 +404,47 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                 const int ncols = min(QCOLS, V - cbase);
                 const float* rowp = stage + tid * SP;
                 auto at = [&](int cc) { return rowp[cc]; };
-                // 0) a row's first pass (empty list): start from the key of the
-                //    smallest of KCAP group maxima of the pass's columns.  At
-                //    least KCAP values reach it, so a key below it is out.
-                constexpr int GS = QCOLS / KCAP;  // columns per group
+                // 0) a row's first pass (empty list): start from a value that at
+                //    least KCAP of the pass's columns reach, so a key below it is
+                //    out.  With room for 2 KCAP groups of 4 or more columns it is
+                //    the KCAP-th largest of their maxima: one group set sorted
+                //    descending, the other ascending, the pairwise maxima are the
+                //    top KCAP of the 2 KCAP (a bitonic split), and their minimum
+                //    is the KCAP-th largest.  Else it is the smallest of KCAP
+                //    group maxima.  (The first takes about a third of the
+                //    candidates of the second on random rows.)
+                constexpr int GS = QCOLS / KCAP;        // columns per group
+                constexpr int GS2 = QCOLS / (2 * KCAP);  // (with 2 KCAP groups)
                 if (GS >= 4 && thr == -INFINITY && ncols == QCOLS) {
                     float mn = INFINITY;
+                    if constexpr (GS2 >= 4) {
+                        float ga[KCAP], gb[KCAP];
 #pragma unroll
-                    for (int gq = 0; gq < KCAP; ++gq) {
-                        float mx = -INFINITY;
+                        for (int gq = 0; gq < 2 * KCAP; ++gq) {
+                            float mx = -INFINITY;
 #pragma unroll
-                        for (int q = 0; q < GS / 4; ++q) {
-                            const f32x4 x = *reinterpret_cast<const f32x4*>(rowp + gq * GS + 4 * q);
-                            mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+                            for (int q = 0; q < GS2 / 4; ++q) {
+                                const f32x4 x = *reinterpret_cast<const f32x4*>(rowp + gq * GS2 + 4 * q);
+                                mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+                            }
+                            if (gq < KCAP) ga[gq] = mx;
+                            else gb[gq - KCAP] = mx;
                         }
-                        mn = fminf(mn, mx);
+                        bitonic_sort<KCAP, true>(ga);
+                        bitonic_sort<KCAP, false>(gb);
+#pragma unroll
+                        for (int i = 0; i < KCAP; ++i) mn = fminf(mn, fmaxf(ga[i], gb[i]));
+                    } else {
+#pragma unroll
+                        for (int gq = 0; gq < KCAP; ++gq) {
+                            float mx = -INFINITY;
+#pragma unroll
+                            for (int q = 0; q < GS / 4; ++q) {
+                                const f32x4 x = *reinterpret_cast<const f32x4*>(rowp + gq * GS + 4 * q);
+                                mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+                            }
+                            mn = fminf(mn, mx);
+                        }
                     }
                     if (mn > -INFINITY && mn < INFINITY)
                         thr = acc_lower_bound(order_key(logit_key_bits(mn, s, c, inv_c)), s, c);
@@ -571,6 +618,118 @@ __global__ __launch_bounds__(256) void lm_topk_merge16_level(const uint64_t* __r
             L[KCAP - 1] = 0;
         }
         if ((lane & 15) == 0 && row < T) out[(row * G2 + blk) * KCAP + r] = best;
+    }
+}
+
+// The whole merge for 16 < G <= 256 groups and k <= 16 in one launch, one
+// workgroup per row, by ranking instead of rounds:
+//  1. The row's top k lies in the lists of the k largest heads (a list whose
+//     head is below the k-th largest head has every entry below k distinct
+//     entries).  Thread t ranks list t's head against all heads (ties of the
+//     16-bit key go to the lower list index, which holds the lower token ids:
+//     groups own increasing column ranges), and the k best lists are kept.
+//  2. Thread 16 s + j holds entry j of kept list s; its rank in the union of
+//     the kept lists is the number of their entries above it (all distinct),
+//     and a rank below k is its output slot.
+template <int KCAP>
+__global__ __launch_bounds__(256) void lm_topk_merge_rank(const uint64_t* __restrict__ part, int T, int G, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ logits) {
+    static_assert(KCAP <= 16, "16 kept lists of at most 16 entries");
+    __shared__ __attribute__((aligned(16))) uint32_t heads[256];
+    __shared__ __attribute__((aligned(16))) uint64_t ent[16][16];
+    __shared__ int sel[16];
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const uint64_t* rp = part + (int64_t)row * G * KCAP;
+    const uint64_t h = tid < G ? rp[(int64_t)tid * KCAP] : 0;
+    // (key + 1, list index reversed): nonzero for a non-empty list
+    const uint32_t hk = h ? ((uint32_t)((h >> 32) + 1) << 8) | (uint32_t)(255 - tid) : 0u;
+    heads[tid] = hk;
+    if (tid < 16) sel[tid] = -1;
+    __syncthreads();
+    int rank = 0;
+#pragma unroll 8
+    for (int u = 0; u < 64; ++u) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(heads + 4 * u);
+        rank += (q[0] > hk) + (q[1] > hk) + (q[2] > hk) + (q[3] > hk);
+    }
+    if (hk && rank < k) sel[rank] = tid;
+    __syncthreads();
+    const int s = tid >> 4, j = tid & 15;
+    const int gs = sel[s];
+    const uint64_t e = (gs >= 0 && j < k) ? rp[(int64_t)gs * KCAP + j] : 0;
+    ent[s][j] = e;
+    const int nz = __syncthreads_count(e != 0);
+    int r = 0;
+#pragma unroll 4
+    for (int q = 0; q < 128; ++q) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&ent[0][0] + 2 * q);
+        const uint64_t a = ((uint64_t)v[1] << 32) | v[0], b = ((uint64_t)v[3] << 32) | v[2];
+        r += (a > e) + (b > e);
+    }
+    if (e != 0 && r < k) {
+        ids[(int64_t)row * k + r] = (int32_t)(~(uint32_t)e);
+        logits[(int64_t)row * k + r] = bf16_bits_to_f32(unorder_key((uint32_t)(e >> 32)));
+    }
+    if (tid >= nz && tid < k) {  // fewer than k entries in all: the rest is empty
+        ids[(int64_t)row * k + tid] = -1;
+        logits[(int64_t)row * k + tid] = -INFINITY;
+    }
+}
+
+// The whole merge for 16 < G <= 256 groups in one launch: one workgroup per
+// row.  Its 16 lane groups (16 lanes each, one DPP row) first take the k best
+// of 16 lists each, as lm_topk_merge16_level does, into LDS; then the first
+// lane group merges those (at most 16) lists as lm_topk_merge16 does.  Only k
+// entries per block are needed: the union of the blocks' top-k lists holds the
+// row's top k.
+template <int KCAP>
+__global__ __launch_bounds__(256) void lm_topk_merge256(const uint64_t* __restrict__ part, int T, int G, int k,
+                                                        int32_t* __restrict__ ids, float* __restrict__ logits) {
+    __shared__ uint64_t blk[16][KCAP];
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int b = tid >> 4, g = tid & 15;
+    const int gi = b * 16 + g;
+    uint64_t L[KCAP];
+    if (gi < G) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(part + ((int64_t)row * G + gi) * KCAP);
+#pragma unroll
+        for (int j = 0; j < KCAP / 2; ++j) {
+            const u32x4 v = src[j];
+            L[2 * j] = ((uint64_t)v[1] << 32) | v[0];
+            L[2 * j + 1] = ((uint64_t)v[3] << 32) | v[2];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KCAP; ++j) L[j] = 0;
+    }
+    for (int r = 0; r < k; ++r) {
+        const uint64_t best = row16_max(L[0]);
+        if (best != 0 && L[0] == best) {
+#pragma unroll
+            for (int j = 0; j < KCAP - 1; ++j) L[j] = L[j + 1];
+            L[KCAP - 1] = 0;
+        }
+        if (g == 0) blk[b][r] = best;
+    }
+    __syncthreads();
+    if (tid >= 16) return;
+    // lane g of the first lane group: block g's list (k entries, zeros past it)
+#pragma unroll
+    for (int j = 0; j < KCAP; ++j) L[j] = j < k ? blk[g][j] : 0;
+    for (int r = 0; r < k; ++r) {
+        const uint64_t best = row16_max(L[0]);
+        if (best != 0 && L[0] == best) {
+#pragma unroll
+            for (int j = 0; j < KCAP - 1; ++j) L[j] = L[j + 1];
+            L[KCAP - 1] = 0;
+        }
+        if (g == 0) {
+            const uint32_t okey = (uint32_t)(best >> 32);
+            ids[(int64_t)row * k + r] = (int32_t)(~(uint32_t)best);
+            logits[(int64_t)row * k + r] = best ? bf16_bits_to_f32(unorder_key(okey)) : -INFINITY;
+        }
     }
 }
 
@@ -837,12 +996,12 @@ static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, in
         launch_tiles<LM_BM, 128, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
     const uint64_t* cur = part;
     int G = p.G;
-    if (G > 16) {
-        // levels of 16 -> 1 until 16 or fewer lists per row remain
+    if (G > 256) {
+        // levels of 16 -> 1 until 256 or fewer lists per row remain
         uint64_t* buf[2];
         buf[0] = part + (size_t)T * (size_t)p.G * KCAP;
         buf[1] = buf[0] + (size_t)T * (size_t)((p.G + 15) / 16) * KCAP;
-        for (int lv = 0; G > 16; ++lv) {
+        for (int lv = 0; G > 256; ++lv) {
             const int G2 = (G + 15) / 16;
             const int64_t vrows = (int64_t)T * G2;
             hipLaunchKernelGGL((lm_topk_merge16_level<KCAP>), dim3((unsigned)((vrows + 15) / 16)), dim3(256), 0, st,
@@ -851,7 +1010,16 @@ static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, in
             G = G2;
         }
     }
-    hipLaunchKernelGGL((lm_topk_merge16<KCAP>), dim3((T + 15) / 16), dim3(256), 0, st, cur, T, G, k, ids, logits);
+    if (G > 16) {
+        if constexpr (KCAP <= 16)
+            hipLaunchKernelGGL((lm_topk_merge_rank<KCAP>), dim3((unsigned)T), dim3(256), 0, st, cur, T, G, k, ids,
+                               logits);
+        else
+            hipLaunchKernelGGL((lm_topk_merge256<KCAP>), dim3((unsigned)T), dim3(256), 0, st, cur, T, G, k, ids,
+                               logits);
+    } else
+        hipLaunchKernelGGL((lm_topk_merge16<KCAP>), dim3((T + 15) / 16), dim3(256), 0, st, cur, T, G, k, ids,
+                           logits);
 }
 
 }  // namespace dflash

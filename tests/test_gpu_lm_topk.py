@@ -146,7 +146,7 @@ def test_skinny_rows_full_vocab(B, full_inputs, T):
     (5, 4099, 256, 8, 0.75, 20.0),     # 8 fragments in flight
     (16, 20000, 384, 64, 0.5, 30.0),   # K steps not a multiple of 8, k = 64
     (13, 1000, 4096, 16, 2.0, 5.0),    # fewer tiles than CUs, 16 fragments in flight
-    (16, 70001, 1024, 32, 1.0, 30.0),  # k = 32, two merge levels
+    (16, 70001, 1024, 32, 1.0, 30.0),  # k = 32, 256 groups: the two-stage merge
 ])
 def test_streaming_rows(B, T, V, Hd, k, s, c):
     H, W = _random_case(T * 31 + V + Hd, T, V, Hd, 0.1)
@@ -162,8 +162,35 @@ def test_skinny_ragged(B, T, V, Hd, k):
     _check(B, H, W, k, 0.75, 20.0, label=f"skinny T{T} V{V} Hd{Hd} k{k}")
 
 
+@pytest.mark.parametrize("T,V,Hd,k", [
+    (200, 40000, 256, 16),  # one row tile, 256 groups of 128 columns: the ranking merge
+    (200, 40000, 256, 32),  # the same with k = 32: the two-stage merge of 16-list blocks
+    (16, 40000, 256, 8),    # the streaming kernel, 256 groups: the ranking merge
+])
+def test_exact_ties_many_groups(B, T, V, Hd, k):
+    """Integer-valued logits (H and W in {-1, 0, 1}, multiplier 1, no cap): the
+    keys are exact on both sides and tie everywhere, so merging more than 16
+    groups must order equal keys by id exactly as the oracle does: every row
+    is an exactly-equal row."""
+    from tests.gpu_common import say
+    rng = np.random.default_rng(T * 3 + V + k)
+    H = WL.to_bf16_bits(rng.integers(-1, 2, (T, Hd)).astype(np.float32))
+    W = WL.to_bf16_bits(rng.integers(-1, 2, (V, Hd)).astype(np.float32))
+    gids, gvals = _run(B, H, W, k, 1.0, 0.0)
+    keys = O.lm_logit_keys(H, W, 1.0, 0.0)
+    exact, near = check_topk_rows(gids, gvals, keys, k, label=f"ties T{T} k{k}")
+    say(f"[lm_topk ties T{T} V{V} k{k}] rows={T} exact={exact} near={near}")
+    assert exact == T
+    # the rows do tie across the cut: at some row, ids outside the list share the k-th key
+    rr = np.arange(T)
+    kth = keys[rr, gids[:, -1]]
+    at_kth = (keys == kth[:, None]).sum(axis=1)
+    in_list = (keys[rr[:, None], gids] == kth[:, None]).sum(axis=1)
+    assert (at_kth > in_list).any()
+
+
 def test_256_rows_full_vocab(B, full_inputs):
     """256 rows over the full vocabulary (one row tile, 256 groups of 256
-    columns, two merge levels): the benchmark's bandwidth-regime launch, every
+    columns, the ranking merge): the benchmark's bandwidth-regime launch, every
     row against the oracle's goldens."""
     _full_rows_vs_golden(B, full_inputs, 0, 256, "256 rows full vocab")
