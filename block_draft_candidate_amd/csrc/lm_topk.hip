@@ -894,7 +894,7 @@ static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p, bool all
     if (allow_skinny && T <= 16 && Hd <= SK_MAXHD && Hd % 128 == 0) {
         // up to 16 rows: one workgroup per CU streams a run of 16-row vocabulary tiles
         const int nK = (int)(Hd / 32);
-        p.skinny_pf = nK % 16 == 0 ? 16 : nK % 8 == 0 ? 8 : 4;
+        p.skinny_pf = nK % 32 == 0 ? 32 : nK % 16 == 0 ? 16 : nK % 8 == 0 ? 8 : 4;
         const int64_t ntiles = (V + 15) / 16;
         int64_t G = ntiles < 256 ? ntiles : 256;
         while (((ntiles + G - 1) / G) * 16 > 65536) ++G;
@@ -982,7 +982,9 @@ static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, in
     if (p.skinny_pf > 0) {
         const float inv_c = c > 0.f ? 1.0f / c : 0.f;
         const dim3 grid((unsigned)p.nwg), block(SK_THREADS);
-        if (p.skinny_pf == 16)
+        if (p.skinny_pf == 32)
+            hipLaunchKernelGGL((lm_topk_skinny<KCAP, 32>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
+        else if (p.skinny_pf == 16)
             hipLaunchKernelGGL((lm_topk_skinny<KCAP, 16>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
         else if (p.skinny_pf == 8)
             hipLaunchKernelGGL((lm_topk_skinny<KCAP, 8>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);

@@ -145,7 +145,8 @@ def test_skinny_rows_full_vocab(B, full_inputs, T):
     (1, 777, 128, 1, 1.0, 0.0),        # one row, 4 fragments in flight, a ragged last tile
     (5, 4099, 256, 8, 0.75, 20.0),     # 8 fragments in flight
     (16, 20000, 384, 64, 0.5, 30.0),   # K steps not a multiple of 8, k = 64
-    (13, 1000, 4096, 16, 2.0, 5.0),    # fewer tiles than CUs, 16 fragments in flight
+    (13, 1000, 4096, 16, 2.0, 5.0),    # fewer tiles than CUs, 32 fragments in flight
+    (9, 3000, 1536, 8, 1.0, 30.0),     # 48 K steps: 16 fragments in flight
     (16, 70001, 1024, 32, 1.0, 30.0),  # k = 32, 256 groups: the two-stage merge
 ])
 def test_streaming_rows(B, T, V, Hd, k, s, c):
