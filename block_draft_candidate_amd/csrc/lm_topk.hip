@@ -734,126 +734,140 @@ __global__ __launch_bounds__(256) void lm_topk_merge256(const uint64_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// lm_topk_skinny: the LM head for at most 16 rows, where the contraction is a
+// lm_topk_stream: the LM head for at most 16 rows, where the contraction is a
 // stream over W with little arithmetic per byte (16 rows: 16 flop per W byte).
 //
-// Workgroup g (one per CU) owns a contiguous run of 16-row vocabulary tiles;
-// its 8 waves take every 8th tile of the run.  A wave streams its tiles' W rows
-// from HBM straight into registers, PF fragments of 16 bytes per lane ahead of
-// the MFMA that uses them (8 waves x PF KB in flight per CU), so no LDS ring
-// and no barrier sits in the stream.  The <= 16 hidden rows are loaded into
-// LDS once (rows padded by 16 bytes, so the 16 rows of a fragment read fall on
-// different banks).  v_mfma_f32_16x16x32_bf16 with the vocabulary rows as M and
-// the hidden rows as N: after a tile's last K step lane (j, g) holds the
-// logits of hidden row j for the tile's vocabulary rows 4g .. 4g + 3; it keys
-// them (scale, cap, bf16) and keeps its own sorted list of the best KCAP keys of
-// row j.  At the end the 32 lists of each row (8 waves x 4 lane groups) are
-// merged in LDS into the group's partial list, the tile kernel's format, and
-// lm_topk_merge16(_level) merge the groups as for the tile kernel.
+// Workgroup g (512 threads, one per CU) owns a contiguous run of 16-row
+// vocabulary tiles, and its 8 waves split the hidden dimension: wave w owns
+// columns [w KW, (w + 1) KW), KW = Hd / 8 = 32 NL.  Per tile a wave reads its
+// 16 x KW slice of W as NL nontemporal loads of 1 KB of row-contiguous bytes
+// (rows read in whole runs: with an MFMA operand layout each load instruction
+// would touch 16 rows at one offset, and that pattern streams ~13% slower),
+// writes it to its own LDS region (16-byte chunks XOR-swizzled by row) and
+// reads it back as v_mfma_f32_16x16x32_bf16 A fragments, vocabulary rows as M;
+// its hidden-row fragments (B, hidden rows as N) sit in registers for the whole
+// stream.  The next tile's loads are issued as soon as the slice is in LDS.
+// The 8 waves' 16 x 16 partial sums meet in LDS (one barrier per tile) and
+// waves 0-3 add them in wave order: thread (w, lane) takes vocabulary row
+// 4 (lane / 16) + w of hidden row lane % 16, keys it (scale, cap, bf16) and
+// keeps its own sorted list of the best KCAP keys.  At the end the 16 lists of
+// each hidden row are merged in LDS into the group's partial list, the tile
+// kernel's format, and the merge kernels finish as for the tile kernel.
 // ---------------------------------------------------------------------------
-constexpr int SK_THREADS = 512;
-constexpr int SK_WAVES = SK_THREADS / 64;
-constexpr int SK_MAXHD = 4096;                  // the hidden rows fill 128 KB of LDS at most
-constexpr int SK_PITCH_PAD = 8;                 // bf16 elements of padding per hidden row
-constexpr int SK_LDS = 16 * (SK_MAXHD + SK_PITCH_PAD);  // elements; also holds the final 16 x 32 x KCAP lists
+constexpr int ST_THREADS = 512;
+constexpr int ST_WAVES = ST_THREADS / 64;
+constexpr int ST_MAXHD = 4096;  // NL <= 16: 64 VGPRs of hidden-row fragments, 16 KB of LDS per wave
 
-template <int KCAP, int PF>
-__global__ __launch_bounds__(SK_THREADS) void lm_topk_skinny(const uint16_t* __restrict__ H,
+// Swizzle of the 16-byte chunks of a row's slice (CPR chunks): chunk c of row r
+// is stored at c ^ st_swz(r), so the 16 rows of a fragment read hit distinct banks.
+template <int CPR>
+__device__ __forceinline__ int st_swz(int r) { return r & (CPR < 16 ? CPR - 1 : 15); }
+
+template <int KCAP, int NL>
+__global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __restrict__ H,
                                                              const uint16_t* __restrict__ W, int T, int V, int Hd,
                                                              int ntiles, int G, float s, float c, float inv_c,
                                                              uint64_t* __restrict__ part) {
-    static_assert(16 * 32 * KCAP * 2 <= SK_LDS, "the row lists fit the LDS of the hidden rows");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[SK_LDS];
+    constexpr int KW = 32 * NL;         // hidden columns per wave
+    constexpr int RB = 2 * KW;          // bytes of one row's slice (a power of two)
+    constexpr int CPR = RB / 16;        // 16-byte chunks per row slice
+    constexpr int WT_BYTES = 16 * RB;   // a wave's slice of one tile: NL KB
+    constexpr int P_FLOATS = ST_WAVES * 4 * 64;  // one tile's partial sums
+    constexpr int STREAM_BYTES = ST_WAVES * WT_BYTES + 2 * P_FLOATS * 4;
+    constexpr int LIST_BYTES = 16 * 16 * KCAP * 4;
+    constexpr int LDS_BYTES = STREAM_BYTES > LIST_BYTES ? STREAM_BYTES : LIST_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = blockIdx.x;
     const int t0 = (int)((int64_t)grp * ntiles / G), t1 = (int)((int64_t)(grp + 1) * ntiles / G);
     const int v0 = t0 * 16;  // the group's first vocabulary row: ids are v0 + column
-    const int pitch = Hd + SK_PITCH_PAD;
+    const int j = lane & 15, q = lane >> 4;
+    const int k0 = wave * KW;
+    uint8_t* wt = lds + wave * WT_BYTES;
+    float* P = reinterpret_cast<float*>(lds + ST_WAVES * WT_BYTES);  // [2][wave][e][lane]
 
-    // the hidden rows (rows >= T read as zero) -> LDS
-    const int c8n = Hd / 8;
-    for (int idx = tid; idx < 16 * c8n; idx += SK_THREADS) {
-        const int r = idx / c8n, c8 = idx - r * c8n;
-        const u32x4 v = r < T ? ldg16(H + (int64_t)r * Hd + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(lds + r * pitch + c8 * 8) = v;
-    }
-    __syncthreads();
-
-    const int j = lane & 15, g = lane >> 4;
-    const int nK = Hd / 32;          // MFMA K steps per tile
-    const int nKB = nK / PF;         // blocks of PF steps per tile
-    const int nt = t1 - t0;
-    const int ntw = nt > wave ? (nt - wave + SK_WAVES - 1) / SK_WAVES : 0;  // this wave's tiles
-    const int nblk = ntw * nKB;
-    // W fragment of lane (j, g) at block b, step i: row (tile's first row + j), columns
-    // 32 (kb + i) + 8 g .. + 8; rows past the vocabulary reload the last row (discarded)
-    auto frag_ptr = [&](int b) {
-        const int bb = min(b, max(nblk - 1, 0));
-        const int tw = bb / nKB;
-        const int kb = (bb - tw * nKB) * PF;
-        const int v = min((t0 + wave + SK_WAVES * tw) * 16 + j, V - 1);
-        return W + (int64_t)v * Hd + kb * 32 + 8 * g;
-    };
-    u32x4 buf[PF];
-    {
-        // issued in the order the loop consumes them (the loop's waits then
-        // leave PF - 1 fragments in flight; issued in another order, the wait
-        // at the loop head would drain them all)
-        const uint16_t* p = frag_ptr(0);
+    // this wave's hidden-row fragments: lane (j, q) holds row j, columns
+    // k0 + 32 s + 8 q .. + 8 of K step s (rows >= T are zero)
+    u32x4 hf[NL];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            buf[i] = ldg16_stream(p + 32 * i);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    for (int st = 0; st < NL; ++st)
+        hf[st] = j < T ? ldg16(H + (int64_t)j * Hd + k0 + 32 * st + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+
+    // load i of a tile slice: bytes [1024 i + 16 lane, + 16) of the wave's
+    // row-major 16 x RB slice, i.e. row (1024 i + 16 lane) / RB; rows past the
+    // vocabulary reload the last row (never keyed)
+    auto wptr = [&](int t, int i) {
+        const int byte = 1024 * i + 16 * lane;
+        const int r = byte / RB, col = (byte % RB) / 2;
+        const int v = min(t * 16 + r, V - 1);
+        return W + (int64_t)v * Hd + k0 + col;
+    };
+    auto lds_slot = [&](int i) {
+        const int byte = 1024 * i + 16 * lane;
+        const int r = byte / RB, cc = (byte % RB) / 16;
+        return wt + r * RB + 16 * (cc ^ st_swz<CPR>(r));
+    };
+
+    const int nt = t1 - t0;
+    u32x4 buf[NL];
+    if (nt > 0) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) buf[i] = ldg16_stream(wptr(t0, i));
     }
     uint32_t L[KCAP];
 #pragma unroll
     for (int e = 0; e < KCAP; ++e) L[e] = 0u;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* hrow = lds + j * pitch + 8 * g;  // B fragment of lane (j, g): hidden row j
-    for (int b = 0; b < nblk; ++b) {
-        const int tw = b / nKB;
-        const int kb = (b - tw * nKB) * PF;
-        const uint16_t* pn = frag_ptr(b + 1);
+
+    for (int tt = 0; tt < nt; ++tt) {
+        const int t = t0 + tt;
+        // the tile's slice -> this wave's LDS region, then the next tile's loads
+        // into the same registers
 #pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            const bf16x8 hb = as_bf16x8(*reinterpret_cast<const u32x4*>(hrow + (kb + i) * 32));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf[i]), hb, acc, 0, 0, 0);
-            buf[i] = ldg16_stream(pn + 32 * i);
+        for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lds_slot(i)) = buf[i];
+        if (tt + 1 < nt) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) buf[i] = ldg16_stream(wptr(t + 1, i));
         }
-        if (kb + PF == nK) {
-            // the tile is done: key its logits of row j and keep the best
-            const int vt = (t0 + wave + SK_WAVES * tw) * 16 + 4 * g;
-            if (j < T) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int v = vt + e;
-                    if (v < V) {
-                        const uint32_t p = (order_key(logit_key_bits(acc[e], s, c, inv_c)) << 16) |
-                                           (0xffffu - (uint32_t)(v - v0));
-                        if (p > L[KCAP - 1]) list_insert<KCAP>(L, p);
-                    }
-                }
+        for (int st = 0; st < NL; ++st) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(wt + j * RB + 16 * ((4 * st + q) ^ st_swz<CPR>(j)));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(hf[st]), acc, 0, 0, 0);
+        }
+        // partial sums -> LDS (double-buffered by tile), one barrier, and waves
+        // 0-3 key the tile: lane l of the MFMA output holds rows 4 (l / 16) + e
+        // of hidden row l % 16
+        float* Pb = P + (tt & 1) * P_FLOATS;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Pb[(wave * 4 + e) * 64 + lane] = acc[e];
+        __syncthreads();
+        if (wave < 4) {
+            float x = 0.f;
+#pragma unroll
+            for (int w = 0; w < ST_WAVES; ++w) x += Pb[(w * 4 + wave) * 64 + lane];
+            const int v = t * 16 + 4 * q + wave;
+            if (j < T && v < V) {
+                const uint32_t p = (order_key(logit_key_bits(x, s, c, inv_c)) << 16) | (0xffffu - (uint32_t)(v - v0));
+                if (p > L[KCAP - 1]) list_insert<KCAP>(L, p);
             }
-            acc = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
 
-    // the 32 lists of each row -> LDS (over the hidden rows), then a 32-lane
-    // merge per row: wave w takes rows w and w + 8 (lanes 0-31 and 32-63)
+    // the 16 lists of each hidden row -> LDS (over the stream's buffers), then a
+    // 16-lane merge per row: wave w < 4 takes rows 4w .. 4w + 3
     __syncthreads();
     uint32_t* lists = reinterpret_cast<uint32_t*>(lds);
-    {
-        uint32_t* dst = lists + ((j * 32) + wave * 4 + g) * KCAP;
+    if (wave < 4) {
+        uint32_t* dst = lists + (j * 16 + wave * 4 + q) * KCAP;
 #pragma unroll
         for (int e = 0; e < KCAP; ++e) dst[e] = L[e];
     }
     __syncthreads();
-    const int row = wave + 8 * (lane >> 5);
-    const int sub = lane & 31;
+    if (wave >= 4) return;
+    const int row = wave * 4 + q;
     {
-        const uint32_t* src = lists + (row * 32 + sub) * KCAP;
+        const uint32_t* src = lists + (row * 16 + j) * KCAP;
 #pragma unroll
         for (int e = 0; e < KCAP; ++e) L[e] = src[e];
     }
@@ -862,13 +876,13 @@ __global__ __launch_bounds__(SK_THREADS) void lm_topk_skinny(const uint16_t* __r
     for (int r = 0; r < KCAP; ++r) {
         uint32_t best = L[0];
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) best = max(best, (uint32_t)__shfl_xor((int)best, off, 32));
+        for (int off = 1; off < 16; off <<= 1) best = max(best, (uint32_t)__shfl_xor((int)best, off, 16));
         if (best != 0u && L[0] == best) {  // keys of one group differ in the column bits: one owner
 #pragma unroll
             for (int e = 0; e < KCAP - 1; ++e) L[e] = L[e + 1];
             L[KCAP - 1] = 0u;
         }
-        if (sub == 0) {
+        if (j == 0) {
             uint64_t e = 0;
             if (best != 0u) {
                 const uint32_t id = (uint32_t)v0 + (0xffffu - (best & 0xffffu));
@@ -883,18 +897,18 @@ struct LmPlan {
     int BM, BN, KCAP, nM, nN, G, xmx;
     int64_t nwg;
     size_t ws;
-    int skinny_pf;  // > 0: lm_topk_skinny with this many fragments in flight per lane
+    int stream_nl;  // > 0: lm_topk_stream with this many 1 KB loads per wave per tile (Hd / 256)
 };
 
-// allow_skinny: the streaming kernel may be used (not with the rank projection
+// allow_stream: the streaming kernel may be used (not with the rank projection
 // riding along, which the tile kernel carries).
-static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p, bool allow_skinny = true) {
+static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p, bool allow_stream = true) {
     p.KCAP = k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
-    p.skinny_pf = 0;
-    if (allow_skinny && T <= 16 && Hd <= SK_MAXHD && Hd % 128 == 0) {
-        // up to 16 rows: one workgroup per CU streams a run of 16-row vocabulary tiles
-        const int nK = (int)(Hd / 32);
-        p.skinny_pf = nK % 32 == 0 ? 32 : nK % 16 == 0 ? 16 : nK % 8 == 0 ? 8 : 4;
+    p.stream_nl = 0;
+    if (allow_stream && T <= 16 && Hd <= ST_MAXHD && Hd % 256 == 0 && ((Hd / 256) & (Hd / 256 - 1)) == 0) {
+        // up to 16 rows: one workgroup per CU streams a run of 16-row vocabulary
+        // tiles, its 8 waves splitting the hidden dimension
+        p.stream_nl = (int)(Hd / 256);
         const int64_t ntiles = (V + 15) / 16;
         int64_t G = ntiles < 256 ? ntiles : 256;
         while (((ntiles + G - 1) / G) * 16 > 65536) ++G;
@@ -979,17 +993,19 @@ template <int KCAP>
 static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, int T, int V, int Hd, int k,
                        float s, float c, uint64_t* part, int32_t* ids, float* logits, const LmProj& pj,
                        hipStream_t st) {
-    if (p.skinny_pf > 0) {
+    if (p.stream_nl > 0) {
         const float inv_c = c > 0.f ? 1.0f / c : 0.f;
-        const dim3 grid((unsigned)p.nwg), block(SK_THREADS);
-        if (p.skinny_pf == 32)
-            hipLaunchKernelGGL((lm_topk_skinny<KCAP, 32>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
-        else if (p.skinny_pf == 16)
-            hipLaunchKernelGGL((lm_topk_skinny<KCAP, 16>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
-        else if (p.skinny_pf == 8)
-            hipLaunchKernelGGL((lm_topk_skinny<KCAP, 8>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
-        else
-            hipLaunchKernelGGL((lm_topk_skinny<KCAP, 4>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, inv_c, part);
+        const dim3 grid((unsigned)p.nwg), block(ST_THREADS);
+        switch (p.stream_nl) {
+#define ST_CASE(n)                                                                                          \
+    case n:                                                                                                 \
+        hipLaunchKernelGGL((lm_topk_stream<KCAP, n>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, \
+                           inv_c, part);                                                                    \
+        break;
+            ST_CASE(1) ST_CASE(2) ST_CASE(4) ST_CASE(8) ST_CASE(16)
+#undef ST_CASE
+            default: break;
+        }
     } else if (p.BM == 64)
         launch_tiles<64, 128, KCAP>(p, H, W, T, V, Hd, s, c, part, pj, st);
     else if (p.BN == 256)
@@ -1040,7 +1056,7 @@ extern "C" size_t dflash_lm_topk_workspace_size(int64_t T, int64_t V, int64_t Hd
 // the launch plan.
 static int lm_topk_validate(const uint16_t* H, const uint16_t* W, int64_t T, int64_t V, int64_t Hd, int32_t k,
                             float output_multiplier, float softcap, int32_t* ids, float* logits, LmPlan& p,
-                            bool allow_skinny) {
+                            bool allow_stream) {
     if (!H || !W || !ids || !logits) return DFLASH_ERR_INVALID_ARG;
     if (!DFLASH_ALIGNED16(H) || !DFLASH_ALIGNED16(W)) return DFLASH_ERR_INVALID_ARG;
     if (T < 1 || V < 1 || Hd < 1 || k < 1 || k > V) return DFLASH_ERR_INVALID_ARG;
@@ -1050,7 +1066,7 @@ static int lm_topk_validate(const uint16_t* H, const uint16_t* W, int64_t T, int
     if (T > INT32_MAX || V > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     // tile buffer ranges and lane offsets (up to 256 rows of Hd bf16) are int32 byte counts
     if ((int64_t)256 * Hd * 2 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
-    if (!lm_plan(T, V, Hd, k, p, allow_skinny)) return DFLASH_ERR_UNSUPPORTED;
+    if (!lm_plan(T, V, Hd, k, p, allow_stream)) return DFLASH_ERR_UNSUPPORTED;
     return DFLASH_OK;
 }
 

@@ -141,13 +141,16 @@ def test_skinny_rows_full_vocab(B, full_inputs, T):
 
 
 @pytest.mark.parametrize("T,V,Hd,k,s,c", [
-    # up to 16 rows with Hd % 128 == 0, Hd <= 4096: the streaming kernel
-    (1, 777, 128, 1, 1.0, 0.0),        # one row, 4 fragments in flight, a ragged last tile
-    (5, 4099, 256, 8, 0.75, 20.0),     # 8 fragments in flight
-    (16, 20000, 384, 64, 0.5, 30.0),   # K steps not a multiple of 8, k = 64
-    (13, 1000, 4096, 16, 2.0, 5.0),    # fewer tiles than CUs, 32 fragments in flight
-    (9, 3000, 1536, 8, 1.0, 30.0),     # 48 K steps: 16 fragments in flight
-    (16, 70001, 1024, 32, 1.0, 30.0),  # k = 32, 256 groups: the two-stage merge
+    # up to 16 rows with Hd / 256 a power of two up to 16: the streaming kernel,
+    # each wave reading Hd / 256 KB of every tile
+    (1, 777, 256, 1, 1.0, 0.0),        # one row, 1 load per wave per tile, a ragged last tile
+    (5, 4099, 512, 8, 0.75, 20.0),     # 2 loads
+    (16, 70001, 1024, 32, 1.0, 30.0),  # 4 loads, k = 32, 256 groups: the two-stage merge
+    (16, 20000, 2048, 64, 0.5, 30.0),  # 8 loads, k = 64
+    (13, 1000, 4096, 16, 2.0, 5.0),    # 16 loads, fewer tiles than CUs
+    # other hidden sizes take the 64-row tile
+    (9, 3000, 1536, 8, 1.0, 30.0),     # Hd / 256 = 6
+    (7, 5000, 384, 8, 0.75, 20.0),     # Hd % 256 != 0
 ])
 def test_streaming_rows(B, T, V, Hd, k, s, c):
     H, W = _random_case(T * 31 + V + Hd, T, V, Hd, 0.1)
