@@ -255,6 +255,13 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+        // Column offset of K slice sl.  With one row tile (WNT) the workgroups
+        // start at different slices (slice sl is read as (sl + krot) mod nK):
+        // in lockstep every workgroup would read its W rows, 8 KB apart, at
+        // one column offset, and such requests crowd a few memory channels.
+        // (Slices past nK stay past it: the prologue's spare slice reads zeros.)
+        const int krot = WNT ? (int)((blockIdx.x >> 3) % (unsigned)nK) : 0;
+        auto kof = [&](int sl) { return (sl < nK ? (sl + krot >= nK ? sl + krot - nK : sl + krot) : sl) * LM_BK; };
         // Fragment q (in the order the MFMAs below consume them: A0, B0..B{NB-1},
         // A1..A{MB-1}) of one 16-wide K step (k16 = 0..3) of the slice whose A
         // and B halves sit in ring slots sa and sb.
@@ -290,9 +297,9 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
             for (int q = 0; q < NQ; ++q) {
                 if (q < NFR && rk16 >= 0) read_frag(ra, rb, rk16, q, na, nb);
                 if (dma == 1 && q < NIA)
-                    dma_one<NIA, TAIL>(rsA, smem + dslot * UNIT, voffA, lcA, wave_s, hd_t, dkt * LM_BK, q);
+                    dma_one<NIA, TAIL>(rsA, smem + dslot * UNIT, voffA, lcA, wave_s, hd_t, kof(dkt), q);
                 if (dma == 2 && q < NIB)
-                    dma_one<NIB, TAIL, WAUX>(rsB, smem + dslot * UNIT, voffB, lcB, wave_s, hd_t, dkt * LM_BK, q);
+                    dma_one<NIB, TAIL, WAUX>(rsB, smem + dslot * UNIT, voffB, lcB, wave_s, hd_t, kof(dkt), q);
             }
             mfmas(fa, fb);
 #pragma unroll
@@ -313,10 +320,10 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
         // an A half (the hidden states, L2/MALL resident) for one.  The wait
         // before each barrier lets exactly the newest B half stay in flight.
         bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
-        dma_slice<NIB, TAIL, WAUX>(rsB, smem + 0 * UNIT, voffB, lcB, wave_s, hd_t, 0);
-        dma_slice<NIA, TAIL>(rsA, smem + 1 * UNIT, voffA, lcA, wave_s, hd_t, 0);
-        dma_slice<NIB, TAIL, WAUX>(rsB, smem + 2 * UNIT, voffB, lcB, wave_s, hd_t, LM_BK);  // past K: zeros, unused
-        dma_slice<NIA, TAIL>(rsA, smem + 3 * UNIT, voffA, lcA, wave_s, hd_t, LM_BK);
+        dma_slice<NIB, TAIL, WAUX>(rsB, smem + 0 * UNIT, voffB, lcB, wave_s, hd_t, kof(0));
+        dma_slice<NIA, TAIL>(rsA, smem + 1 * UNIT, voffA, lcA, wave_s, hd_t, kof(0));
+        dma_slice<NIB, TAIL, WAUX>(rsB, smem + 2 * UNIT, voffB, lcB, wave_s, hd_t, kof(1));  // past K: zeros, unused
+        dma_slice<NIA, TAIL>(rsA, smem + 3 * UNIT, voffA, lcA, wave_s, hd_t, kof(1));
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(NIB + NIA));  // slice 0 landed
         __builtin_amdgcn_s_barrier();
         compiler_fence();
