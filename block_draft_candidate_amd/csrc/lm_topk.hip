@@ -741,7 +741,7 @@ __global__ __launch_bounds__(256) void lm_topk_merge256(const uint64_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// lm_topk_stream: the LM head for at most 16 rows, where the contraction is a
+// lm_topk_stream: the LM head for at most 32 rows, where the contraction is a
 // stream over W with little arithmetic per byte (16 rows: 16 flop per W byte).
 //
 // Workgroup g (512 threads, one per CU) owns a contiguous run of 16-row
@@ -752,37 +752,41 @@ __global__ __launch_bounds__(256) void lm_topk_merge256(const uint64_t* __restri
 // would touch 16 rows at one offset, and that pattern streams ~13% slower),
 // writes it to its own LDS region (16-byte chunks XOR-swizzled by row) and
 // reads it back as v_mfma_f32_16x16x32_bf16 A fragments, vocabulary rows as M;
-// its hidden-row fragments (B, hidden rows as N) sit in registers for the whole
-// stream.  The next tile's loads are issued as soon as the slice is in LDS.
-// The 8 waves' 16 x 16 partial sums meet in LDS (one barrier per tile) and
-// waves 0-3 add them in wave order: thread (w, lane) takes vocabulary row
-// 4 (lane / 16) + w of hidden row lane % 16, keys it (scale, cap, bf16) and
-// keeps its own sorted list of the best KCAP keys.  At the end the 16 lists of
-// each hidden row are merged in LDS into the group's partial list, the tile
-// kernel's format, and the merge kernels finish as for the tile kernel.
+// its hidden-row fragments (B, hidden rows as N; NBH blocks of 16 rows) sit in
+// registers for the whole stream.  The next tile's loads are issued as soon as
+// the slice is in LDS.  The 8 waves' 16 x 16 partial sums (per hidden block)
+// meet in LDS (one barrier per tile) and waves 0 .. 4 NBH - 1 add them in wave
+// order: thread (w, lane) takes vocabulary row 4 (lane / 16) + w % 4 of hidden
+// row 16 (w / 4) + lane % 16, keys it (scale, cap, bf16) and keeps its own
+// sorted list of the best KCAP keys.  At the end the 16 lists of each hidden
+// row are merged in LDS into the group's partial list, the tile kernel's
+// format, and the merge kernels finish as for the tile kernel.
 // ---------------------------------------------------------------------------
 constexpr int ST_THREADS = 512;
 constexpr int ST_WAVES = ST_THREADS / 64;
-constexpr int ST_MAXHD = 4096;  // NL <= 16: 64 VGPRs of hidden-row fragments, 16 KB of LDS per wave
+constexpr int ST_MAXHD = 4096;  // NL <= 16: 64 VGPRs of hidden-row fragments per block, 16 KB of LDS per wave
 
 // Swizzle of the 16-byte chunks of a row's slice (CPR chunks): chunk c of row r
 // is stored at c ^ st_swz(r), so the 16 rows of a fragment read hit distinct banks.
 template <int CPR>
 __device__ __forceinline__ int st_swz(int r) { return r & (CPR < 16 ? CPR - 1 : 15); }
 
-template <int KCAP, int NL>
+template <int KCAP, int NL, int NBH>
 __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __restrict__ H,
                                                              const uint16_t* __restrict__ W, int T, int V, int Hd,
                                                              int ntiles, int G, float s, float c, float inv_c,
                                                              uint64_t* __restrict__ part) {
+    static_assert(NBH == 1 || NBH == 2, "16 or 32 hidden rows");
     constexpr int KW = 32 * NL;         // hidden columns per wave
     constexpr int RB = 2 * KW;          // bytes of one row's slice (a power of two)
     constexpr int CPR = RB / 16;        // 16-byte chunks per row slice
     constexpr int WT_BYTES = 16 * RB;   // a wave's slice of one tile: NL KB
-    constexpr int P_FLOATS = ST_WAVES * 4 * 64;  // one tile's partial sums
+    constexpr int NE = 4 * NBH;         // partial sums per lane per tile
+    constexpr int P_FLOATS = ST_WAVES * NE * 64;  // one tile's partial sums
     constexpr int STREAM_BYTES = ST_WAVES * WT_BYTES + 2 * P_FLOATS * 4;
-    constexpr int LIST_BYTES = 16 * 16 * KCAP * 4;
+    constexpr int LIST_BYTES = 16 * NBH * 16 * KCAP * 4;
     constexpr int LDS_BYTES = STREAM_BYTES > LIST_BYTES ? STREAM_BYTES : LIST_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -794,12 +798,15 @@ __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __r
     uint8_t* wt = lds + wave * WT_BYTES;
     float* P = reinterpret_cast<float*>(lds + ST_WAVES * WT_BYTES);  // [2][wave][e][lane]
 
-    // this wave's hidden-row fragments: lane (j, q) holds row j, columns
-    // k0 + 32 s + 8 q .. + 8 of K step s (rows >= T are zero)
-    u32x4 hf[NL];
+    // this wave's hidden-row fragments: lane (j, q) of block b holds row 16 b + j,
+    // columns k0 + 32 s + 8 q .. + 8 of K step s (rows >= T are zero)
+    u32x4 hf[NBH][NL];
 #pragma unroll
-    for (int st = 0; st < NL; ++st)
-        hf[st] = j < T ? ldg16(H + (int64_t)j * Hd + k0 + 32 * st + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+    for (int hb = 0; hb < NBH; ++hb)
+#pragma unroll
+        for (int st = 0; st < NL; ++st)
+            hf[hb][st] = 16 * hb + j < T ? ldg16(H + (int64_t)(16 * hb + j) * Hd + k0 + 32 * st + 8 * q)
+                                         : u32x4{0u, 0u, 0u, 0u};
 
     // load i of a tile slice: bytes [1024 i + 16 lane, + 16) of the wave's
     // row-major 16 x RB slice, i.e. row (1024 i + 16 lane) / RB; rows past the
@@ -825,6 +832,10 @@ __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __r
     uint32_t L[KCAP];
 #pragma unroll
     for (int e = 0; e < KCAP; ++e) L[e] = 0u;
+    // the keying thread's output: hidden row 16 (wave / 4) + j, vocabulary row
+    // 4 q + wave % 4 of each tile (waves 0 .. 4 NBH - 1)
+    const bool keyer = wave < 4 * NBH;
+    const int krow = 16 * (wave >> 2) + j, kvr = 4 * q + (wave & 3);
 
     for (int tt = 0; tt < nt; ++tt) {
         const int t = t0 + tt;
@@ -836,25 +847,31 @@ __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __r
 #pragma unroll
             for (int i = 0; i < NL; ++i) buf[i] = ldg16_stream(wptr(t + 1, i));
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[NBH];
+#pragma unroll
+        for (int hb = 0; hb < NBH; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < NL; ++st) {
             const u32x4 a = *reinterpret_cast<const u32x4*>(wt + j * RB + 16 * ((4 * st + q) ^ st_swz<CPR>(j)));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(hf[st]), acc, 0, 0, 0);
+#pragma unroll
+            for (int hb = 0; hb < NBH; ++hb)
+                acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(hf[hb][st]), acc[hb], 0, 0, 0);
         }
-        // partial sums -> LDS (double-buffered by tile), one barrier, and waves
-        // 0-3 key the tile: lane l of the MFMA output holds rows 4 (l / 16) + e
-        // of hidden row l % 16
+        // partial sums -> LDS (double-buffered by tile), one barrier, and the
+        // keying waves add them in wave order: lane l of block b's MFMA output
+        // holds vocabulary rows 4 (l / 16) + e of hidden row 16 b + l % 16
         float* Pb = P + (tt & 1) * P_FLOATS;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Pb[(wave * 4 + e) * 64 + lane] = acc[e];
+        for (int hb = 0; hb < NBH; ++hb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Pb[(wave * NE + 4 * hb + e) * 64 + lane] = acc[hb][e];
         __syncthreads();
-        if (wave < 4) {
+        if (keyer) {
             float x = 0.f;
 #pragma unroll
-            for (int w = 0; w < ST_WAVES; ++w) x += Pb[(w * 4 + wave) * 64 + lane];
-            const int v = t * 16 + 4 * q + wave;
-            if (j < T && v < V) {
+            for (int w = 0; w < ST_WAVES; ++w) x += Pb[(w * NE + wave) * 64 + lane];
+            const int v = t * 16 + kvr;
+            if (krow < T && v < V) {
                 const uint32_t p = (order_key(logit_key_bits(x, s, c, inv_c)) << 16) | (0xffffu - (uint32_t)(v - v0));
                 if (p > L[KCAP - 1]) list_insert<KCAP>(L, p);
             }
@@ -862,16 +879,16 @@ __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __r
     }
 
     // the 16 lists of each hidden row -> LDS (over the stream's buffers), then a
-    // 16-lane merge per row: wave w < 4 takes rows 4w .. 4w + 3
+    // 16-lane merge per row: wave w < 4 NBH takes rows 4w .. 4w + 3
     __syncthreads();
     uint32_t* lists = reinterpret_cast<uint32_t*>(lds);
-    if (wave < 4) {
-        uint32_t* dst = lists + (j * 16 + wave * 4 + q) * KCAP;
+    if (keyer) {
+        uint32_t* dst = lists + (krow * 16 + kvr) * KCAP;
 #pragma unroll
         for (int e = 0; e < KCAP; ++e) dst[e] = L[e];
     }
     __syncthreads();
-    if (wave >= 4) return;
+    if (!keyer) return;
     const int row = wave * 4 + q;
     {
         const uint32_t* src = lists + (row * 16 + j) * KCAP;
@@ -905,6 +922,7 @@ struct LmPlan {
     int64_t nwg;
     size_t ws;
     int stream_nl;  // > 0: lm_topk_stream with this many 1 KB loads per wave per tile (Hd / 256)
+    int stream_nbh;  // its 16-row blocks of hidden rows (1 or 2)
 };
 
 // allow_stream: the streaming kernel may be used (not with the rank projection
@@ -912,10 +930,14 @@ struct LmPlan {
 static bool lm_plan(int64_t T, int64_t V, int64_t Hd, int k, LmPlan& p, bool allow_stream = true) {
     p.KCAP = k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
     p.stream_nl = 0;
-    if (allow_stream && T <= 16 && Hd <= ST_MAXHD && Hd % 256 == 0 && ((Hd / 256) & (Hd / 256 - 1)) == 0) {
-        // up to 16 rows: one workgroup per CU streams a run of 16-row vocabulary
-        // tiles, its 8 waves splitting the hidden dimension
+    if (allow_stream && T <= 32 && Hd <= ST_MAXHD && Hd % 256 == 0 && ((Hd / 256) & (Hd / 256 - 1)) == 0 &&
+        (T <= 16 || p.KCAP <= 16)) {
+        // up to 32 rows: one workgroup per CU streams a run of 16-row vocabulary
+        // tiles, its 8 waves splitting the hidden dimension (above 16 rows with
+        // KCAP <= 16: the hidden-row fragments of 32 rows and longer lists would
+        // not fit the registers together)
         p.stream_nl = (int)(Hd / 256);
+        p.stream_nbh = T > 16 ? 2 : 1;
         const int64_t ntiles = (V + 15) / 16;
         int64_t G = ntiles < 256 ? ntiles : 256;
         while (((ntiles + G - 1) / G) * 16 > 65536) ++G;
@@ -1004,10 +1026,14 @@ static void launch_all(const LmPlan& p, const uint16_t* H, const uint16_t* W, in
         const float inv_c = c > 0.f ? 1.0f / c : 0.f;
         const dim3 grid((unsigned)p.nwg), block(ST_THREADS);
         switch (p.stream_nl) {
-#define ST_CASE(n)                                                                                          \
-    case n:                                                                                                 \
-        hipLaunchKernelGGL((lm_topk_stream<KCAP, n>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, c, \
-                           inv_c, part);                                                                    \
+#define ST_CASE(n)                                                                                             \
+    case n:                                                                                                    \
+        if (p.stream_nbh == 1)                                                                                 \
+            hipLaunchKernelGGL((lm_topk_stream<KCAP, n, 1>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, \
+                               c, inv_c, part);                                                                \
+        else if constexpr (KCAP <= 16)                                                                         \
+            hipLaunchKernelGGL((lm_topk_stream<KCAP, n, 2>), grid, block, 0, st, H, W, T, V, Hd, p.nN, p.G, s, \
+                               c, inv_c, part);                                                                \
         break;
             ST_CASE(1) ST_CASE(2) ST_CASE(4) ST_CASE(8) ST_CASE(16)
 #undef ST_CASE

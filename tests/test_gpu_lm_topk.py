@@ -141,13 +141,16 @@ def test_skinny_rows_full_vocab(B, full_inputs, T):
 
 
 @pytest.mark.parametrize("T,V,Hd,k,s,c", [
-    # up to 16 rows with Hd / 256 a power of two up to 16: the streaming kernel,
-    # each wave reading Hd / 256 KB of every tile
+    # up to 32 rows (k <= 16 above 16 rows) with Hd / 256 a power of two up to 16:
+    # the streaming kernel, each wave reading Hd / 256 KB of every tile
     (1, 777, 256, 1, 1.0, 0.0),        # one row, 1 load per wave per tile, a ragged last tile
     (5, 4099, 512, 8, 0.75, 20.0),     # 2 loads
     (16, 70001, 1024, 32, 1.0, 30.0),  # 4 loads, k = 32, 256 groups: the two-stage merge
     (16, 20000, 2048, 64, 0.5, 30.0),  # 8 loads, k = 64
     (13, 1000, 4096, 16, 2.0, 5.0),    # 16 loads, fewer tiles than CUs
+    (24, 9000, 4096, 16, 0.75, 20.0),  # 17-32 rows: two 16-row blocks of hidden rows
+    (32, 70001, 1024, 8, 1.0, 30.0),   # 32 rows, 4 loads
+    (20, 5000, 2048, 32, 0.5, 30.0),   # 17-32 rows with k > 16: the 64-row tile
     # other hidden sizes take the 64-row tile
     (9, 3000, 1536, 8, 1.0, 30.0),     # Hd / 256 = 6
     (7, 5000, 384, 8, 0.75, 20.0),     # Hd % 256 != 0
