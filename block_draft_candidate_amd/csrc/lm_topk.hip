@@ -23,6 +23,8 @@
 //   * Row slices and groups are blocked per XCD (workgroup ids go to XCDs
 //     round-robin), so each XCD's L2 serves W tiles to several row slices and
 //     H slices to several groups.
+//   * Up to 32 rows (k <= 16 above 16 rows) with Hd / 256 a power of two up to
+//     16, lm_topk_stream replaces the tiles: the head is then a stream over W.
 //   * A merge kernel picks the k best of the groups' partial lists per row:
 //     16 lanes per row up to 16 groups, a workgroup per row up to 256 groups
 //     (beyond that, after launches that merge blocks of 16 lists).
