@@ -74,3 +74,36 @@ def test_step_in_a_graph(B):
         for name, t, r in zip(("ids", "logits", "hp", "edges", "cache", "out"), (ids, logits, hp, edges, cache, out),
                               ref):
             assert torch.equal(t, r), f"replay {rep}: {name} differs from the eager result"
+
+
+def test_streaming_lm_topk_in_a_graph(B):
+    """The LM head at 16 rows (the streaming kernel and the ranking merge) captured
+    in a graph: every replay equals the eager call bit for bit."""
+    import torch
+    from tests.gpu_common import dev_bf16
+    rng = np.random.default_rng(5)
+    T, V, Hd, k = 16, 20000, 1024, 16
+    H = dev_bf16(WL.to_bf16_bits(rng.standard_normal((T, Hd), dtype=np.float32)))
+    W = dev_bf16(WL.to_bf16_bits(rng.standard_normal((V, Hd), dtype=np.float32) * np.float32(0.1)))
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    logits = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.lm_topk_workspace_size(T, V, Hd, k), dtype=torch.uint8, device="cuda")
+    B.lm_topk(H, W, k, 0.5, 30.0, ids, logits, ws)
+    torch.cuda.synchronize()
+    ref = (ids.clone(), logits.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.lm_topk(H, W, k, 0.5, 30.0, ids, logits, ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.lm_topk(H, W, k, 0.5, 30.0, ids, logits, ws, stream=s)
+    for rep in range(3):
+        ids.zero_()
+        logits.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ref[0]) and torch.equal(logits, ref[1]), f"replay {rep} differs from the eager call"

@@ -157,7 +157,10 @@ def test_skinny_rows_full_vocab(B, full_inputs, T):
 ])
 def test_streaming_rows(B, T, V, Hd, k, s, c):
     H, W = _random_case(T * 31 + V + Hd, T, V, Hd, 0.1)
-    _check(B, H, W, k, s, c, label=f"streaming T{T} V{V} Hd{Hd} k{k}")
+    gids, gvals = _check(B, H, W, k, s, c, label=f"streaming T{T} V{V} Hd{Hd} k{k}")
+    # deterministic: a second call gives the same bits
+    gids2, gvals2 = _run(B, H, W, k, s, c)
+    assert np.array_equal(gids, gids2) and np.array_equal(gvals.view(np.uint32), gvals2.view(np.uint32))
 
 
 @pytest.mark.parametrize("T,V,Hd,k", [
