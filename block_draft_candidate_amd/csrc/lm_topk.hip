@@ -30,6 +30,7 @@
 //     (beyond that, after launches that merge blocks of 16 lists).
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 
@@ -75,36 +76,68 @@ __device__ __forceinline__ float cap_tanh(float y) {
     return copysignf(a < 0.55f ? tp : te, y);
 }
 
+// fp32 -> bf16 bits, round to nearest even; a NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_key_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rne;
+}
+
 // The top-k key of one accumulator: bf16(c * tanh(s * acc / c)), or bf16(s * acc)
-// without a cap.
+// without a cap (c = 0; c is uniform) ...
 __device__ __forceinline__ uint32_t logit_key_bits(float acc, float s, float c, float inv_c) {
     float x = s * acc;
-    if (c > 0.f) x = c * cap_tanh(x * inv_c);  // c is uniform
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // fp32 -> bf16, round to nearest even
-    return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rne;  // NaN stays a quiet NaN
+    if (c > 0.f) x = c * cap_tanh(x * inv_c);
+    return bf16_key_bits(x);
+}
+// ... and the same with the cap setting known at compile time.
+template <bool CAP>
+__device__ __forceinline__ uint32_t logit_key_bits_as(float acc, float s, float c, float inv_c) {
+    float x = s * acc;
+    if constexpr (CAP) x = c * cap_tanh(x * inv_c);
+    return bf16_key_bits(x);
+}
+
+// atanh for |z| < 0.9 in fp32, within about 1e-6 relative: the odd series
+// through z^13 below |z| = 0.25 (the first dropped term is under 3e-10 of the
+// sum), above it half the natural log of (1 + |z|) / (1 - |z|), a ratio of at
+// least 5/3 whose hardware log2 and reciprocal err by about an ulp each.  Both
+// forms are evaluated and one is selected.
+__device__ __forceinline__ float bound_atanh(float z) {
+    const float a = fabsf(z);
+    const float q = a * a;
+    float p = 1.f / 13.f;
+    p = fmaf(p, q, 1.f / 11.f);
+    p = fmaf(p, q, 1.f / 9.f);
+    p = fmaf(p, q, 1.f / 7.f);
+    p = fmaf(p, q, 1.f / 5.f);
+    p = fmaf(p, q, 1.f / 3.f);
+    const float ts = fmaf(a * q, p, a);
+    const float tl = 0.34657359027997264f * __builtin_amdgcn_logf((1.f + a) * __builtin_amdgcn_rcpf(1.f - a));
+    return copysignf(a < 0.25f ? ts : tl, z);
 }
 
 // A raw-accumulator bound below which a logit's key is certainly smaller than
 // the key `okey`: a logit that rounds to the key or above lies above the bf16
 // value one step below it, which is mapped back through the cap and the scale
-// with a relative margin of 2^-12 at each step (far above the fp32 error of
-// the tanh and atanh used).  Near saturation of the cap (|x| > 0.9 c) no bound
-// is used.
-__device__ float acc_lower_bound(uint32_t okey, float s, float c) {
+// (products with the reciprocals 1 / c and 1 / s) with a relative margin of
+// 2^-12 at each step, far above the few-ulp error of those products, of the
+// atanh above and of the kernel's tanh.  Near saturation of the cap
+// (|x| > 0.9 c) no bound is used.
+__device__ __forceinline__ float acc_lower_bound(uint32_t okey, float inv_s, float c, float inv_c) {
     if (okey < 0x0081u) return -INFINITY;  // the step below is -inf: nothing to bound
     const float xlo = bf16_bits_to_f32(unorder_key(okey - 1));
     if (!(xlo > -INFINITY)) return -INFINITY;
     float y = xlo;
     if (c > 0.f) {
-        const float z = xlo / c;
+        const float z = xlo * inv_c;
         if (!(fabsf(z) < 0.9f)) return -INFINITY;
-        y = c * atanhf(z);
+        y = c * bound_atanh(z);
     }
     y -= fabsf(y) * 0x1p-12f + 1e-30f;
-    float a = y / s;
+    float a = y * inv_s;
     a -= fabsf(a) * 0x1p-12f + 1e-30f;
-    return a;
+    return a == a ? a : -INFINITY;  // (an overflow to +inf leaves inf - inf)
 }
 
 // Insert p into the descending list L (the smallest falls off).  A no-op when
@@ -120,6 +153,36 @@ __device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t p) {
 #pragma unroll
     for (int j = N - 1; j > 0; --j) L[j] = med3_u32(L[j], L[j - 1], p);
     L[0] = max(L[0], p);
+}
+
+// Position of the lowest set bit, ~0u for zero (v_ffbl_b32 as such: written
+// as a select around a count of trailing zeros it is not always folded).
+__device__ __forceinline__ uint32_t ffbl(uint32_t x) {
+    uint32_t r;
+    asm("v_ffbl_b32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+// m &= m - 1 over MW 32-bit words read as one number, word 0 least
+// significant: clears its lowest set bit (a subtract-with-borrow chain).
+template <int MW>
+__device__ __forceinline__ void clear_lowest_bit(uint32_t (&m)[MW]) {
+    if constexpr (MW == 4) {
+        unsigned __int128 x = ((unsigned __int128)(((uint64_t)m[3] << 32) | m[2]) << 64) | (((uint64_t)m[1] << 32) | m[0]);
+        x &= x - 1;
+        m[0] = (uint32_t)x;
+        m[1] = (uint32_t)(x >> 32);
+        m[2] = (uint32_t)(x >> 64);
+        m[3] = (uint32_t)(x >> 96);
+    } else if constexpr (MW == 2) {
+        uint64_t x = ((uint64_t)m[1] << 32) | m[0];
+        x &= x - 1;
+        m[0] = (uint32_t)x;
+        m[1] = (uint32_t)(x >> 32);
+    } else {
+        static_assert(MW == 1, "mask of 1, 2 or 4 words");
+        m[0] &= m[0] - 1u;
+    }
 }
 
 // Bitonic sort of N (a power of two) values in registers, descending if DESC.
@@ -201,6 +264,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
 #pragma unroll
     for (int j = 0; j < KCAP; ++j) list[j] = 0u;
     float thr = -INFINITY;
+    const float inv_s = 1.0f / s;  // (s > 0: checked on the host)
 
     const int nK = (Hd + LM_BK - 1) / LM_BK;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
@@ -456,7 +520,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                         }
                     }
                     if (mn > -INFINITY && mn < INFINITY)
-                        thr = acc_lower_bound(order_key(logit_key_bits(mn, s, c, inv_c)), s, c);
+                        thr = acc_lower_bound(order_key(logit_key_bits(mn, s, c, inv_c)), inv_s, c, inv_c);
                 }
                 // 1) mask of this row's columns whose raw accumulator reaches the
                 //    threshold (16-byte reads, no divergence)
@@ -481,34 +545,63 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lm_topk_tiles(
                     if (valid < 32) mw &= valid == 0 ? 0u : ~((1u << (32 - valid)) - 1u);
                     m[w] = mw;
                 }
-                // 2) candidates in column (= token id) order, one per lane per
-                //    round, the LDS read of the next one issued ahead; the
-                //    threshold is raised once per pass, after the rounds.
-                auto pop = [&]() {  // lowest remaining column (highest bit of the lowest word)
-                    int cc = -1;
+                // 2) candidates, one per lane per round, the LDS read of the next
+                //    one issued ahead; the threshold is raised once per pass,
+                //    after the rounds.  The list is kept under a strict total
+                //    order, so the order of the inserts does not change it.
+                // pop: the lowest set bit of the mask read as one MW-word number
+                // (word 0 least significant), found as the smallest of the
+                // words' lowest set bits offset by 32 w (a zero word gives ~0u,
+                // which the OR keeps), and cleared by m &= m - 1 over all words
+                // (a borrow chain, no branch).  Bit b of word w is column
+                // 32 w + 31 - b, i.e. position ^ 31; none left gives -32.
+                auto pop = [&]() {
+                    uint32_t pos = ~0u;
 #pragma unroll
-                    for (int w = MW - 1; w >= 0; --w)
-                        if (m[w]) cc = 32 * w + __builtin_clz(m[w]);
-                    if (cc >= 0) m[cc >> 5] &= ~(0x80000000u >> (cc & 31));
-                    return cc;
+                    for (int w = 0; w < MW; ++w) pos = min(pos, ffbl(m[w]) | (uint32_t)(32 * w));
+                    clear_lowest_bit<MW>(m);
+                    return (int)(pos ^ 31u);
                 };
                 bool changed = false;
-                int cc = pop();
-                float v = at(cc < 0 ? 0 : cc);
                 // (the threshold does not move inside a pass, so every masked
                 // candidate is evaluated; the insert is a no-op for a key below
-                // the list, and the round body has no branch)
-                while (cc >= 0) {
-                    const int cn = pop();
-                    const float vn = at(cn < 0 ? 0 : cn);
-                    const uint32_t kb = logit_key_bits(v, s, c, inv_c);
-                    const uint32_t p = (order_key(kb) << 16) | (0xffffu - (uint32_t)(cbase + cc - gcol0));
-                    changed |= p > list[KCAP - 1];
-                    list_insert(list, p);
-                    cc = cn;
-                    v = vn;
+                // the list, and the round body has no branch.)  Up to 16
+                // entries the loop is compiled once per cap setting, which is
+                // uniform; with longer lists that costs spilled registers, and
+                // the cap stays a uniform branch inside the key function.
+                auto rounds = [&](auto cap) {
+                    int cc = pop();
+                    float v = at(cc < 0 ? 0 : cc);
+                    while (cc >= 0) {
+                        const int cn = pop();
+                        const float vn = at(cn < 0 ? 0 : cn);
+                        const uint32_t kb = logit_key_bits_as<decltype(cap)::value>(v, s, c, inv_c);
+                        const uint32_t p = (order_key(kb) << 16) | (0xffffu - (uint32_t)(cbase + cc - gcol0));
+                        changed |= p > list[KCAP - 1];
+                        list_insert(list, p);
+                        cc = cn;
+                        v = vn;
+                    }
+                };
+                if constexpr (KCAP > 16) {
+                    int cc = pop();
+                    float v = at(cc < 0 ? 0 : cc);
+                    while (cc >= 0) {
+                        const int cn = pop();
+                        const float vn = at(cn < 0 ? 0 : cn);
+                        const uint32_t kb = logit_key_bits(v, s, c, inv_c);
+                        const uint32_t p = (order_key(kb) << 16) | (0xffffu - (uint32_t)(cbase + cc - gcol0));
+                        changed |= p > list[KCAP - 1];
+                        list_insert(list, p);
+                        cc = cn;
+                        v = vn;
+                    }
+                } else if (c > 0.f) {
+                    rounds(std::integral_constant<bool, true>{});
+                } else {
+                    rounds(std::integral_constant<bool, false>{});
                 }
-                if (changed && list[KCAP - 1] != 0u) thr = acc_lower_bound(list[KCAP - 1] >> 16, s, c);
+                if (changed && list[KCAP - 1] != 0u) thr = acc_lower_bound(list[KCAP - 1] >> 16, inv_s, c, inv_c);
             }
             if (row_ok() && mixed) {
                 // the mixed tile's projection columns V .. V + R - 1 (R % 4 == 0,
