@@ -727,27 +727,39 @@ __global__ __launch_bounds__(256) void lm_topk_merge16_level(const uint64_t* __r
 // workgroup per row, by ranking instead of rounds:
 //  1. The row's top k lies in the lists of the k largest heads (a list whose
 //     head is below the k-th largest head has every entry below k distinct
-//     entries).  Thread t ranks list t's head against all heads (ties of the
-//     16-bit key go to the lower list index, which holds the lower token ids:
-//     groups own increasing column ranges), and the k best lists are kept.
-//  2. Thread 16 s + j holds entry j of kept list s; its rank in the union of
-//     the kept lists is the number of their entries above it (all distinct),
-//     and a rank below k is its output slot.
+//     entries).  Thread t loads list t whole and ranks its head against all
+//     heads (ties of the 16-bit key go to the lower list index, which holds
+//     the lower token ids: groups own increasing column ranges); the k best
+//     lists go to LDS in head order, so no second load from memory is needed.
+//  2. Thread 16 s + j holds entry j of kept list s.  Its rank in the union of
+//     the kept lists is the number of their entries above it (all distinct):
+//     in each sorted list that count comes from a binary search (in its own
+//     list it is j), and a rank below k is its output slot.
 template <int KCAP>
 __global__ __launch_bounds__(256) void lm_topk_merge_rank(const uint64_t* __restrict__ part, int T, int G, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ logits) {
     static_assert(KCAP <= 16, "16 kept lists of at most 16 entries");
     __shared__ __attribute__((aligned(16))) uint32_t heads[256];
     __shared__ __attribute__((aligned(16))) uint64_t ent[16][16];
-    __shared__ int sel[16];
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
-    const uint64_t* rp = part + (int64_t)row * G * KCAP;
-    const uint64_t h = tid < G ? rp[(int64_t)tid * KCAP] : 0;
+    uint64_t L[KCAP];
+    if (tid < G) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(part + ((int64_t)row * G + tid) * KCAP);
+#pragma unroll
+        for (int j = 0; j < KCAP / 2; ++j) {
+            const u32x4 v = src[j];
+            L[2 * j] = ((uint64_t)v[1] << 32) | v[0];
+            L[2 * j + 1] = ((uint64_t)v[3] << 32) | v[2];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KCAP; ++j) L[j] = 0;
+    }
     // (key + 1, list index reversed): nonzero for a non-empty list
-    const uint32_t hk = h ? ((uint32_t)((h >> 32) + 1) << 8) | (uint32_t)(255 - tid) : 0u;
+    const uint32_t hk = L[0] ? ((uint32_t)((L[0] >> 32) + 1) << 8) | (uint32_t)(255 - tid) : 0u;
     heads[tid] = hk;
-    if (tid < 16) sel[tid] = -1;
+    ent[tid >> 4][tid & 15] = 0;  // slots of lists not kept (and past KCAP) stay empty
     __syncthreads();
     int rank = 0;
 #pragma unroll 8
@@ -755,19 +767,27 @@ __global__ __launch_bounds__(256) void lm_topk_merge_rank(const uint64_t* __rest
         const u32x4 q = *reinterpret_cast<const u32x4*>(heads + 4 * u);
         rank += (q[0] > hk) + (q[1] > hk) + (q[2] > hk) + (q[3] > hk);
     }
-    if (hk && rank < k) sel[rank] = tid;
+    if (hk && rank < k) {
+        // entries at list position k or later have k entries above them
+#pragma unroll
+        for (int j = 0; j < KCAP; ++j) ent[rank][j] = j < k ? L[j] : 0;
+    }
     __syncthreads();
     const int s = tid >> 4, j = tid & 15;
-    const int gs = sel[s];
-    const uint64_t e = (gs >= 0 && j < k) ? rp[(int64_t)gs * KCAP + j] : 0;
-    ent[s][j] = e;
+    const uint64_t e = ent[s][j];
     const int nz = __syncthreads_count(e != 0);
+    // count of entries above e in each descending list of 16: steps of 8, 4, 2,
+    // 1 leave it exact except that 15 may still be 16
     int r = 0;
-#pragma unroll 4
-    for (int q = 0; q < 128; ++q) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&ent[0][0] + 2 * q);
-        const uint64_t a = ((uint64_t)v[1] << 32) | v[0], b = ((uint64_t)v[3] << 32) | v[2];
-        r += (a > e) + (b > e);
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+        const uint64_t* a = ent[s2];
+        int c = a[7] > e ? 8 : 0;
+        c += a[c + 3] > e ? 4 : 0;
+        c += a[c + 1] > e ? 2 : 0;
+        c += a[c] > e ? 1 : 0;
+        c += (c == 15 && a[15] > e) ? 1 : 0;
+        r += c;
     }
     if (e != 0 && r < k) {
         ids[(int64_t)row * k + r] = (int32_t)(~(uint32_t)e);
