@@ -152,6 +152,7 @@ def test_skinny_rows_full_vocab(B, full_inputs, T):
     (32, 70001, 1024, 8, 1.0, 30.0),   # 32 rows, 4 loads
     (17, 3000, 512, 16, 0.75, 5.0),    # one row in the second hidden block
     (3, 5, 256, 4, 1.0, 0.0),          # a vocabulary smaller than one tile
+    (2, 291, 256, 16, 1.0, 30.0),      # 19 groups: the ranking merge with a 3-entry last list
     (20, 5000, 2048, 32, 0.5, 30.0),   # 17-32 rows with k > 16: the 64-row tile
     # other hidden sizes take the 64-row tile
     (9, 3000, 1536, 8, 1.0, 30.0),     # Hd / 256 = 6
