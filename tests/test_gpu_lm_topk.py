@@ -54,6 +54,11 @@ def _random_case(seed, T, V, Hd, sigma_w):
     (1, 777, 8, 1, 1.0, 0.0),           # one row, k = 1, a single K chunk
     (37, 4099, 72, 64, 2.0, 30.0),      # k = 64, V just past a tile
     (513, 20000, 136, 16, 0.5, 30.0),   # three row tiles, two partial
+    # 256-row tiles with 64-entry lists (k in (32, 64])
+    (2048, 8320, 72, 64, 0.75, 20.0),   # 8 row tiles x 32 groups of 256-column tiles, a K tail
+    (1024, 16640, 128, 48, 1.0, 30.0),  # 4 row tiles x 64 groups of 256-column tiles
+    (100, 9000, 256, 48, 1.0, 30.0),    # one row tile of 128-column tiles (nontemporal W, rotated K order)
+    (300, 20000, 200, 40, 0.5, 0.0),    # two row tiles of 128-column tiles, no cap
 ])
 def test_ragged_shapes(B, T, V, Hd, k, s, c):
     H, W = _random_case(T * 7 + V, T, V, Hd, 0.2)
