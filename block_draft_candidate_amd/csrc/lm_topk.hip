@@ -932,8 +932,8 @@ __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __r
         const int v = min(t * 16 + r, V - 1);
         return W + (int64_t)v * Hd + k0 + col;
     };
-    auto lds_slot = [&](int i) {
-        const int byte = 1024 * i + 16 * lane;
+    auto lds_slot = [&](int i, int ln) {
+        const int byte = 1024 * i + 16 * ln;
         const int r = byte / RB, cc = (byte % RB) / 16;
         return wt + r * RB + 16 * (cc ^ st_swz<CPR>(r));
     };
@@ -954,10 +954,17 @@ __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __r
 
     for (int tt = 0; tt < nt; ++tt) {
         const int t = t0 + tt;
+        // LDS addresses from an opaque copy of the lane, so that they are
+        // recomputed per tile: hoisted out of the loop they hold ~30 registers,
+        // and with 32 hidden rows the kernel then spills inside the loop, where
+        // each reload waits for the next tile's loads in flight
+        int lane_t = lane;
+        asm volatile("" : "+v"(lane_t));
+        const int jt = lane_t & 15, qt = lane_t >> 4;
         // the tile's slice -> this wave's LDS region, then the next tile's loads
         // into the same registers
 #pragma unroll
-        for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lds_slot(i)) = buf[i];
+        for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lds_slot(i, lane_t)) = buf[i];
         if (tt + 1 < nt) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) buf[i] = ldg16_stream(wptr(t + 1, i));
@@ -967,7 +974,7 @@ __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __r
         for (int hb = 0; hb < NBH; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < NL; ++st) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(wt + j * RB + 16 * ((4 * st + q) ^ st_swz<CPR>(j)));
+            const u32x4 a = *reinterpret_cast<const u32x4*>(wt + jt * RB + 16 * ((4 * st + qt) ^ st_swz<CPR>(jt)));
 #pragma unroll
             for (int hb = 0; hb < NBH; ++hb)
                 acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(hf[hb][st]), acc[hb], 0, 0, 0);
@@ -979,12 +986,12 @@ __global__ __launch_bounds__(ST_THREADS) void lm_topk_stream(const uint16_t* __r
 #pragma unroll
         for (int hb = 0; hb < NBH; ++hb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Pb[(wave * NE + 4 * hb + e) * 64 + lane] = acc[hb][e];
+            for (int e = 0; e < 4; ++e) Pb[(wave * NE + 4 * hb + e) * 64 + lane_t] = acc[hb][e];
         __syncthreads();
         if (keyer) {
             float x = 0.f;
 #pragma unroll
-            for (int w = 0; w < ST_WAVES; ++w) x += Pb[(w * NE + wave) * 64 + lane];
+            for (int w = 0; w < ST_WAVES; ++w) x += Pb[(w * NE + wave) * 64 + lane_t];
             const int v = t * 16 + kvr;
             if (krow < T && v < V) {
                 const uint32_t p = (order_key(logit_key_bits(x, s, c, inv_c)) << 16) | (0xffffu - (uint32_t)(v - v0));
