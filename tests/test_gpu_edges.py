@@ -58,19 +58,24 @@ def test_large_workload_subset(B):
     check_edges(E, _ref(d), d["U"], "large")
 
 
-def test_large_full_size_sampled_requests(B):
+def test_large_full_size_all_requests(B):
     """The large configuration at its full 512 x 16 rows, the launch the
     benchmark times (two K slices of the projection, the k = 32 / rank 256
-    bilinear tile); the oracle checks whole requests spread over the batch."""
+    bilinear tile); the oracle checks every request, 64 at a time."""
+    from tests.gpu_common import say
     d = WL.candidate_inputs("large")
     Rq, S = d["requests"], d["steps"]
     E = _gpu_edges(B, d)
     assert E.shape == d["ids"].shape + (d["top_k"],)
-    g = np.random.default_rng(17)
-    req = np.unique(np.concatenate([[0, 1, Rq - 1], g.integers(0, Rq, 9)]))
-    rows = (req[:, None] * S + np.arange(S)).reshape(-1)
-    ref = O.candidate_edges(d["P"], d["S"], d["ids"][req], d["U"][req], d["H"][rows], d["Wp"], d["anchor"][req])
-    check_edges(E[req], ref, d["U"][req], "large, full size")
+    hp = O.rank_projection(d["H"], d["Wp"]).reshape(Rq, S, -1)
+    worst = 0.0
+    for r0 in range(0, Rq, 64):
+        req = np.arange(r0, min(Rq, r0 + 64))
+        ref = O.candidate_edges_from_hp(d["P"], d["S"], d["ids"][req], d["U"][req],
+                                        hp[req].reshape(len(req) * S, -1), d["anchor"][req])
+        check_edges(E[req], ref, d["U"][req], f"large, full size, requests {r0}..{req[-1]}")
+        worst = max(worst, float(np.abs(E[req] - ref).max()))
+    say(f"[edges large full size] {Rq} requests, max|dE|={worst:.3g}")
 
 
 @pytest.mark.parametrize("Rq,S,k,V,R,Hd", [
